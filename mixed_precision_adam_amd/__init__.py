@@ -1,0 +1,209 @@
+"""Python binding of libzero_shard.so: one data-parallel rank's ZeRO step on MI355X.
+
+Argument marshalling only.  Every function has the name of the C entry point
+it wraps (declared in include/zero_shard.h); all device work runs in the HIP
+kernels of ``csrc/zero_shard.hip``.  PyTorch supplies device memory and the
+stream.  There is no fallback: if the library is missing, importing this
+package raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzero_shard.so")
+
+ZERO_BF16 = 0
+ZERO_FP16 = 1
+ZERO_OK, ZERO_ERR_INVALID, ZERO_ERR_CAPACITY, ZERO_ERR_HIP = 0, -1, -2, -3
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m mixed_precision_adam_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+# PyTorch's HIP runtime must be the one the library binds to (it owns the memory and streams the library
+# is handed), so it is loaded first; the library's libamdhip64.so.7 dependency then resolves to it.
+import torch  # noqa: E402,F401
+
+
+def hip_runtimes_loaded() -> list:
+    """Distinct libamdhip64 files mapped into this process (exactly one is allowed)."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64" in line:
+                paths.add(os.path.realpath(line.split()[-1]))
+    return sorted(paths)
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class zero_layout(C.Structure):
+    _fields_ = [("psi", C.c_int64), ("padded_numel", C.c_int64), ("shard_numel", C.c_int64),
+                ("shard_offset", C.c_int64), ("shard_valid", C.c_int64), ("world", C.c_int32), ("rank", C.c_int32),
+                ("bytes_dp", C.c_int64), ("bytes_zero1", C.c_int64), ("bytes_zero2", C.c_int64),
+                ("bytes_zero3", C.c_int64)]
+
+
+class zero_segment(C.Structure):
+    _fields_ = [("tensor", C.c_int32), ("reserved", C.c_int32), ("src_offset", C.c_int64),
+                ("dst_offset", C.c_int64), ("numel", C.c_int64)]
+
+
+class zero_flat_seg(C.Structure):
+    _fields_ = [("src", C.c_void_p), ("src_offset", C.c_int64), ("dst_offset", C.c_int64), ("numel", C.c_int64)]
+
+
+class zero_adamw_hparams(C.Structure):
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double), ("eps", C.c_double),
+                ("weight_decay", C.c_double), ("grad_scale", C.c_double), ("step", C.c_int64)]
+
+
+_P = C.c_void_p
+_lib = C.CDLL(LIB_PATH)
+if len(hip_runtimes_loaded()) != 1:
+    raise ImportError(f"more than one HIP runtime in this process: {hip_runtimes_loaded()}")
+_lib.zero_last_error.restype = C.c_char_p
+_lib.zero_shard_layout.argtypes = [_P, C.c_int32, C.c_int32, C.c_int32, C.POINTER(zero_layout), _P, C.c_int32,
+                                   C.POINTER(C.c_int32)]
+_lib.zero_flatten_plan.argtypes = [_P, C.c_int32, _P, C.c_int32, _P]
+_lib.zero_flatten_grads.argtypes = [_P, C.c_int32, C.c_int, _P, C.c_int64, _P]
+_lib.zero_grad_sqnorm_workspace_bytes.argtypes = [C.c_int64]
+_lib.zero_grad_sqnorm_workspace_bytes.restype = C.c_size_t
+_lib.zero_grad_sqnorm.argtypes = [_P, C.c_int, C.c_int64, _P, C.c_size_t, _P, _P, _P]
+_lib.zero_step_decision.argtypes = [_P, _P, C.c_int32, C.c_double, C.POINTER(C.c_double), C.POINTER(C.c_int32),
+                                    C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_int32), C.POINTER(C.c_double)]
+_lib.zero_clip_coef.argtypes = [C.c_double, C.c_double]
+_lib.zero_clip_coef.restype = C.c_double
+_lib.zero_loss_scale_update.argtypes = [C.POINTER(C.c_double), C.c_int32, C.POINTER(C.c_int32), C.c_int32]
+_lib.zero_cosine_lr.argtypes = [C.c_int64, C.c_int64, C.c_double, C.c_double]
+_lib.zero_cosine_lr.restype = C.c_double
+_lib.zero_adamw_step.argtypes = [_P, C.c_int, _P, _P, _P, _P, C.c_int64, C.POINTER(zero_adamw_hparams), _P]
+
+# Every symbol include/zero_shard.h declares.
+EXPORTS = ("zero_last_error", "zero_shard_layout", "zero_flatten_plan", "zero_flatten_grads",
+           "zero_grad_sqnorm_workspace_bytes", "zero_grad_sqnorm", "zero_step_decision", "zero_clip_coef",
+           "zero_loss_scale_update", "zero_cosine_lr", "zero_adamw_step")
+
+
+def library() -> C.CDLL:
+    return _lib
+
+
+def zero_last_error() -> str:
+    return _lib.zero_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != ZERO_OK:
+        raise ZeroError(status, zero_last_error())
+
+
+def _addr(x) -> int | None:
+    """Device address of a torch tensor, or an int address as is."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+@dataclass
+class Layout:
+    psi: int
+    padded_numel: int
+    shard_numel: int
+    shard_offset: int
+    shard_valid: int
+    world: int
+    rank: int
+    bytes_dp: int
+    bytes_zero1: int
+    bytes_zero2: int
+    bytes_zero3: int
+
+
+def zero_shard_layout(numels, world: int, rank: int):
+    """Returns (Layout, segments) where segments is a ctypes array of zero_segment."""
+    arr = (C.c_int64 * max(len(numels), 1))(*[int(n) for n in numels])
+    out = zero_layout()
+    n = C.c_int32(0)
+    st = _lib.zero_shard_layout(C.cast(arr, _P), len(numels), world, rank, C.byref(out), None, 0, C.byref(n))
+    if st not in (ZERO_OK, ZERO_ERR_CAPACITY):
+        _check(st)
+    segs = (zero_segment * max(n.value, 1))()
+    _check(_lib.zero_shard_layout(C.cast(arr, _P), len(numels), world, rank, C.byref(out), C.cast(segs, _P),
+                                  n.value, C.byref(n)))
+    lay = Layout(*(getattr(out, f) for f, _ in zero_layout._fields_))
+    return lay, segs[:n.value]
+
+
+def zero_flatten_plan(segments, tensor_ptrs) -> bytes:
+    """Packs segments + tensor base addresses into the 32-byte device descriptors (returned as bytes)."""
+    n = len(segments)
+    segs = (zero_segment * max(n, 1))(*segments)
+    ptrs = (C.c_void_p * max(len(tensor_ptrs), 1))(*[_addr(p) for p in tensor_ptrs])
+    out = (zero_flat_seg * max(n, 1))()
+    _check(_lib.zero_flatten_plan(C.cast(segs, _P), n, C.cast(ptrs, _P), len(tensor_ptrs), C.cast(out, _P)))
+    return bytes(out)[: n * C.sizeof(zero_flat_seg)]
+
+
+def zero_flatten_grads(segs_dev, n_segs: int, dtype: int, shard, shard_numel: int, stream=None) -> None:
+    _check(_lib.zero_flatten_grads(_addr(segs_dev), n_segs, dtype, _addr(shard), shard_numel, _stream(stream)))
+
+
+def zero_grad_sqnorm_workspace_bytes(n: int) -> int:
+    return int(_lib.zero_grad_sqnorm_workspace_bytes(n))
+
+
+def zero_grad_sqnorm(shard, dtype: int, n: int, ws, ws_bytes: int, sqnorm_out, nonfinite_out, stream=None) -> None:
+    _check(_lib.zero_grad_sqnorm(_addr(shard), dtype, n, _addr(ws), ws_bytes, _addr(sqnorm_out),
+                                 _addr(nonfinite_out), _stream(stream)))
+
+
+def zero_step_decision(rank_sqnorms, rank_flags, max_norm: float, loss_scale: float, good_steps: int,
+                       growth_interval: int) -> dict:
+    n = len(rank_sqnorms)
+    sq = (C.c_double * n)(*[float(x) for x in rank_sqnorms])
+    fl = (C.c_int32 * n)(*[int(x) for x in rank_flags])
+    ls, gd = C.c_double(loss_scale), C.c_int32(good_steps)
+    gs, sk, gn = C.c_double(0.0), C.c_int32(0), C.c_double(0.0)
+    _check(_lib.zero_step_decision(C.cast(sq, _P), C.cast(fl, _P), n, max_norm, C.byref(ls), C.byref(gd),
+                                   growth_interval, C.byref(gs), C.byref(sk), C.byref(gn)))
+    return dict(grad_scale=gs.value, skip=sk.value, global_norm=gn.value, loss_scale=ls.value, good_steps=gd.value)
+
+
+def zero_clip_coef(global_sqnorm: float, max_norm: float) -> float:
+    return _lib.zero_clip_coef(global_sqnorm, max_norm)
+
+
+def zero_loss_scale_update(scale: float, nonfinite: int, good_steps: int, growth_interval: int):
+    s, g = C.c_double(scale), C.c_int32(good_steps)
+    _check(_lib.zero_loss_scale_update(C.byref(s), nonfinite, C.byref(g), growth_interval))
+    return s.value, g.value
+
+
+def zero_cosine_lr(t: int, total: int, lr_max: float, lr_min: float) -> float:
+    return _lib.zero_cosine_lr(t, total, lr_max, lr_min)
+
+
+def zero_adamw_step(grad, dtype: int, master, m, v, param, n: int, *, lr: float, beta1: float, beta2: float,
+                    eps: float, weight_decay: float, grad_scale: float, step: int, stream=None) -> None:
+    hp = zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, grad_scale, step)
+    _check(_lib.zero_adamw_step(_addr(grad), dtype, _addr(master), _addr(m), _addr(v), _addr(param), n,
+                                C.byref(hp), _stream(stream)))

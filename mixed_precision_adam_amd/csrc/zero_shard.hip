@@ -1,0 +1,634 @@
+// zero_shard.hip -- libzero_shard.so: one data-parallel rank's share of a
+// ZeRO-1/2/3 mixed-precision AdamW step, written for CDNA4 (gfx950).
+//
+// The operations and their sources are documented in include/zero_shard.h.
+// Design for the MI355X: every device kernel here streams HBM (the AdamW step
+// moves 28 bytes per parameter for ~60 VALU instructions), so the kernels are
+// built around 16-byte coalesced vector accesses, one tile per workgroup with
+// all loads of a tile issued before any arithmetic, and no matrix cores --
+// nothing on this path is a contraction.  The gradient norm is a fixed-grid,
+// fixed-tree fp64 reduction (wavefront shuffles, then LDS) so its bits do not
+// change from run to run.  Floating-point contraction is off for the whole
+// file: the AdamW update is specified as a sequence of individually rounded
+// fp32 operations.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <limits>
+
+#include "zero_shard.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+// ------------------------------------------------------------------ errors
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(ZERO_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+  return ZERO_OK;
+}
+
+constexpr int64_t kMaxPsi = std::numeric_limits<int64_t>::max() / 32;  // 2^58: keeps 16·Ψ and N·S in range
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 256;  // 4 wavefronts of 64
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------------------------ 16-bit formats
+
+// Widen one 16-bit value (in the low half of h) to fp32; exact for both formats.
+template <int DT>
+__device__ __forceinline__ float widen(uint32_t h) {
+  if constexpr (DT == ZERO_BF16) {
+    return __uint_as_float(h << 16);
+  } else {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+  }
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ------------------------------------------------------------------ AdamW
+
+struct AdamScalars {
+  float b1, omb1, b2, omb2, eps, decay, step_size, bc2_sqrt, gscale;
+};
+
+// One element of the update, each line one rounded fp32 operation.
+__device__ __forceinline__ void adam_element(float g, float& p, float& m, float& v, const AdamScalars& s) {
+  g = g * s.gscale;
+  const float m_keep = s.b1 * m;
+  const float m_add = s.omb1 * g;
+  m = m_keep + m_add;
+  const float gg = g * g;
+  const float v_keep = s.b2 * v;
+  const float v_add = s.omb2 * gg;
+  v = v_keep + v_add;
+  float d = sqrtf(v);
+  d = d / s.bc2_sqrt;
+  d = d + s.eps;
+  float u = m / d;
+  u = s.step_size * u;
+  const float p_dec = p * s.decay;
+  p = p_dec - u;
+}
+
+// Vector path: thread handles 8 consecutive elements per tile row (one 16-B
+// grad vector, two 16-B vectors of each fp32 array, one 16-B param vector).
+// A workgroup owns UNROLL·256·8 consecutive elements; all of its loads are
+// issued before the arithmetic so each wave keeps 7·UNROLL 16-B loads in
+// flight.
+template <int DT, int UNROLL>
+__global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const u32x4* __restrict__ grad, f32x4* __restrict__ master,
+                                                           f32x4* __restrict__ mom, f32x4* __restrict__ var,
+                                                           u32x4* __restrict__ param, int64_t n8, AdamScalars s) {
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * (kBlock * UNROLL) + threadIdx.x;
+  u32x4 g[UNROLL];
+  f32x4 p[UNROLL][2], m[UNROLL][2], v[UNROLL][2];
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t i = first + static_cast<int64_t>(u) * kBlock;
+    if (i < n8) {
+      g[u] = grad[i];
+      p[u][0] = master[2 * i];
+      p[u][1] = master[2 * i + 1];
+      m[u][0] = mom[2 * i];
+      m[u][1] = mom[2 * i + 1];
+      v[u][0] = var[2 * i];
+      v[u][1] = var[2 * i + 1];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < UNROLL; ++u) {
+    const int64_t i = first + static_cast<int64_t>(u) * kBlock;
+    if (i < n8) {
+      u32x4 out;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int h = w >> 1;       // which of the two fp32 vectors
+        const int c = (w & 1) * 2;  // first component inside it
+        float p0 = p[u][h][c], p1 = p[u][h][c + 1];
+        float m0 = m[u][h][c], m1 = m[u][h][c + 1];
+        float v0 = v[u][h][c], v1 = v[u][h][c + 1];
+        adam_element(widen<DT>(g[u][w] & 0xFFFFu), p0, m0, v0, s);
+        adam_element(widen<DT>(g[u][w] >> 16), p1, m1, v1, s);
+        p[u][h][c] = p0;
+        p[u][h][c + 1] = p1;
+        m[u][h][c] = m0;
+        m[u][h][c + 1] = m1;
+        v[u][h][c] = v0;
+        v[u][h][c + 1] = v1;
+        out[w] = bf16_rne(p0) | (bf16_rne(p1) << 16);
+      }
+      master[2 * i] = p[u][0];
+      master[2 * i + 1] = p[u][1];
+      mom[2 * i] = m[u][0];
+      mom[2 * i + 1] = m[u][1];
+      var[2 * i] = v[u][0];
+      var[2 * i + 1] = v[u][1];
+      param[i] = out;
+    }
+  }
+}
+
+// Element path for ragged tails and unaligned buffers: the same update, one
+// element per thread, grid-stride.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void adamw_scalar_kernel(const uint16_t* __restrict__ grad,
+                                                              float* __restrict__ master, float* __restrict__ mom,
+                                                              float* __restrict__ var, uint16_t* __restrict__ param,
+                                                              int64_t n, AdamScalars s) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
+    float p = master[i], m = mom[i], v = var[i];
+    adam_element(widen<DT>(grad[i]), p, m, v, s);
+    master[i] = p;
+    mom[i] = m;
+    var[i] = v;
+    param[i] = static_cast<uint16_t>(bf16_rne(p));
+  }
+}
+
+constexpr int kAdamUnroll = 2;
+
+// ------------------------------------------------------------------ gradient square-norm
+
+constexpr int64_t kNormElemsPerPart = int64_t(1) << 16;
+constexpr int64_t kNormMaxParts = 4096;
+
+int64_t norm_parts(int64_t n) {
+  int64_t parts = (n + kNormElemsPerPart - 1) / kNormElemsPerPart;
+  if (parts < 1) parts = 1;
+  if (parts > kNormMaxParts) parts = kNormMaxParts;
+  return parts;
+}
+
+template <int DT>
+__device__ __forceinline__ void accumulate(uint32_t h, double& acc, uint32_t& bad) {
+  constexpr uint32_t kExp = DT == ZERO_BF16 ? 0x7F80u : 0x7C00u;
+  const double x = static_cast<double>(widen<DT>(h));
+  const double sq = x * x;  // exact: at most 2·11 significant bits
+  acc = acc + sq;
+  bad |= ((h & kExp) == kExp) ? 1u : 0u;
+}
+
+// Sum over the workgroup in a fixed tree: butterfly inside each wavefront,
+// then the four wavefront sums in order.  Result valid in thread 0.
+__device__ __forceinline__ void block_reduce(double& acc, uint32_t& bad) {
+  __shared__ double wsum[kBlock / 64];
+  __shared__ uint32_t wbad[kBlock / 64];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    acc = acc + __shfl_xor(acc, off, 64);
+    bad |= __shfl_xor(bad, off, 64);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    wsum[wave] = acc;
+    wbad[wave] = bad;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    acc = wsum[0];
+    bad = wbad[0];
+#pragma unroll
+    for (int w = 1; w < kBlock / 64; ++w) {
+      acc = acc + wsum[w];
+      bad |= wbad[w];
+    }
+  }
+}
+
+// Stage 1: workgroup b reduces its contiguous range of 16-B vectors; the last
+// workgroup also takes the unaligned head and ragged tail elements.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void sqnorm_partial_kernel(const uint16_t* __restrict__ x, int64_t n,
+                                                                int64_t head, int64_t n8, int64_t per_block,
+                                                                double* __restrict__ part_sum,
+                                                                uint32_t* __restrict__ part_bad) {
+  double acc = 0.0;
+  uint32_t bad = 0;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x + head);
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * per_block;
+  const int64_t hi = lo + per_block < n8 ? lo + per_block : n8;
+  constexpr int kU = 4;
+  int64_t i = lo + threadIdx.x;
+  for (; i + (kU - 1) * kBlock < hi; i += kU * kBlock) {
+    u32x4 w[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) w[u] = xv[i + u * kBlock];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        accumulate<DT>(w[u][c] & 0xFFFFu, acc, bad);
+        accumulate<DT>(w[u][c] >> 16, acc, bad);
+      }
+    }
+  }
+  for (; i < hi; i += kBlock) {
+    const u32x4 w = xv[i];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      accumulate<DT>(w[c] & 0xFFFFu, acc, bad);
+      accumulate<DT>(w[c] >> 16, acc, bad);
+    }
+  }
+  if (blockIdx.x == gridDim.x - 1) {
+    for (int64_t j = threadIdx.x; j < head; j += kBlock) accumulate<DT>(x[j], acc, bad);
+    for (int64_t j = head + 8 * n8 + threadIdx.x; j < n; j += kBlock) accumulate<DT>(x[j], acc, bad);
+  }
+  block_reduce(acc, bad);
+  if (threadIdx.x == 0) {
+    part_sum[blockIdx.x] = acc;
+    part_bad[blockIdx.x] = bad;
+  }
+}
+
+// Stage 2: one workgroup folds the partials in a fixed order.
+__global__ __launch_bounds__(kBlock) void sqnorm_final_kernel(const double* __restrict__ part_sum,
+                                                              const uint32_t* __restrict__ part_bad, int64_t parts,
+                                                              double* __restrict__ out_sum,
+                                                              int32_t* __restrict__ out_bad) {
+  double acc = 0.0;
+  uint32_t bad = 0;
+  for (int64_t j = threadIdx.x; j < parts; j += kBlock) {
+    acc = acc + part_sum[j];
+    bad |= part_bad[j];
+  }
+  block_reduce(acc, bad);
+  if (threadIdx.x == 0) {
+    *out_sum = acc;
+    *out_bad = bad ? 1 : 0;
+  }
+}
+
+// ------------------------------------------------------------------ flatten
+
+// A workgroup copies len 16-bit elements from s to d.  When both addresses
+// share their position inside a 16-byte line, a scalar head brings d to a
+// 16-byte boundary and the body moves 16-byte vectors.
+__device__ void copy_piece(const uint16_t* __restrict__ s, uint16_t* __restrict__ d, int64_t len) {
+  const uintptr_t ds = reinterpret_cast<uintptr_t>(d), ss = reinterpret_cast<uintptr_t>(s);
+  int64_t head = len, nv = 0;
+  if (((ds ^ ss) & 15u) == 0) {
+    head = static_cast<int64_t>(((16u - (ds & 15u)) & 15u) >> 1);
+    if (head > len) head = len;
+    nv = (len - head) >> 3;
+  }
+  for (int64_t j = threadIdx.x; j < head; j += kBlock) d[j] = s[j];
+  const u32x4* sv = reinterpret_cast<const u32x4*>(s + head);
+  u32x4* dv = reinterpret_cast<u32x4*>(d + head);
+  constexpr int kU = 4;
+  int64_t j = threadIdx.x;
+  for (; j + (kU - 1) * kBlock < nv; j += kU * kBlock) {
+    u32x4 w[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) w[u] = sv[j + u * kBlock];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) dv[j + u * kBlock] = w[u];
+  }
+  for (; j < nv; j += kBlock) dv[j] = sv[j];
+  for (int64_t t = head + 8 * nv + threadIdx.x; t < len; t += kBlock) d[t] = s[t];
+}
+
+__device__ void zero_piece(uint16_t* __restrict__ d, int64_t len) {
+  const uintptr_t ds = reinterpret_cast<uintptr_t>(d);
+  int64_t head = static_cast<int64_t>(((16u - (ds & 15u)) & 15u) >> 1);
+  if (head > len) head = len;
+  const int64_t nv = (len - head) >> 3;
+  for (int64_t j = threadIdx.x; j < head; j += kBlock) d[j] = 0;
+  u32x4* dv = reinterpret_cast<u32x4*>(d + head);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t j = threadIdx.x; j < nv; j += kBlock) dv[j] = z;
+  for (int64_t t = head + 8 * nv + threadIdx.x; t < len; t += kBlock) d[t] = 0;
+}
+
+// Workgroup b writes shard elements [b·per_block, (b+1)·per_block): it finds
+// the first descriptor that ends past its start by binary search, then walks
+// the descriptors in order, copying covered pieces and zero-filling gaps.
+__global__ __launch_bounds__(kBlock) void flatten_kernel(const zero_flat_seg* __restrict__ segs, int32_t n_segs,
+                                                         uint16_t* __restrict__ shard, int64_t shard_numel,
+                                                         int64_t per_block) {
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * per_block;
+  const int64_t hi = lo + per_block < shard_numel ? lo + per_block : shard_numel;
+  int32_t a = 0, b = n_segs;
+  while (a < b) {
+    const int32_t mid = (a + b) >> 1;
+    if (segs[mid].dst_offset + segs[mid].numel > lo) {
+      b = mid;
+    } else {
+      a = mid + 1;
+    }
+  }
+  int32_t k = a;
+  int64_t pos = lo;
+  while (pos < hi) {
+    if (k < n_segs && segs[k].dst_offset <= pos) {
+      const zero_flat_seg sg = segs[k];
+      int64_t end = sg.dst_offset + sg.numel;
+      if (end > hi) end = hi;
+      if (end > pos) {
+        const uint16_t* src = static_cast<const uint16_t*>(sg.src) + (sg.src_offset + (pos - sg.dst_offset));
+        copy_piece(src, shard + pos, end - pos);
+        pos = end;
+      }
+      ++k;
+    } else {
+      int64_t end = hi;
+      if (k < n_segs && segs[k].dst_offset < end) end = segs[k].dst_offset;
+      zero_piece(shard + pos, end - pos);
+      pos = end;
+    }
+  }
+}
+
+int64_t flatten_per_block(int64_t shard_numel) {
+  constexpr int64_t kMin = 8192, kTargetBlocks = 4096;
+  int64_t per = (shard_numel + kTargetBlocks - 1) / kTargetBlocks;
+  per = (per + kMin - 1) / kMin * kMin;
+  return per < kMin ? kMin : per;
+}
+
+bool dtype_ok(int dt) { return dt == ZERO_BF16 || dt == ZERO_FP16; }
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+const char* zero_last_error(void) { return g_last_error; }
+
+int zero_shard_layout(const int64_t* numels, int32_t n_tensors, int32_t world, int32_t rank, zero_layout* out,
+                      zero_segment* segs, int32_t segs_cap, int32_t* n_segs) {
+  if (!out || !n_segs) return fail(ZERO_ERR_INVALID, "zero_shard_layout: out and n_segs must not be NULL");
+  if (n_tensors < 0 || (n_tensors > 0 && !numels))
+    return fail(ZERO_ERR_INVALID, "zero_shard_layout: bad tensor list (n_tensors=%d)", n_tensors);
+  if (world < 1 || rank < 0 || rank >= world)
+    return fail(ZERO_ERR_INVALID, "zero_shard_layout: rank %d outside world %d", rank, world);
+  if (segs_cap < 0 || (segs_cap > 0 && !segs))
+    return fail(ZERO_ERR_INVALID, "zero_shard_layout: bad segment array (cap=%d)", segs_cap);
+  int64_t psi = 0;
+  for (int32_t t = 0; t < n_tensors; ++t) {
+    if (numels[t] < 0 || numels[t] > kMaxPsi - psi)
+      return fail(ZERO_ERR_INVALID, "zero_shard_layout: tensor %d numel %lld invalid or total too large", t,
+                  static_cast<long long>(numels[t]));
+    psi += numels[t];
+  }
+  const int64_t shard = (psi + world - 1) / world;
+  const int64_t begin = static_cast<int64_t>(rank) * shard;
+  const int64_t stop = begin + shard < psi ? begin + shard : psi;  // end of real (unpadded) elements
+  zero_layout L{};
+  L.psi = psi;
+  L.padded_numel = static_cast<int64_t>(world) * shard;
+  L.shard_numel = shard;
+  L.shard_offset = begin;
+  L.shard_valid = stop > begin ? stop - begin : 0;
+  L.world = world;
+  L.rank = rank;
+  L.bytes_dp = 16 * psi;                                   // 2 param + 2 grad + 12 optimizer, all replicated
+  L.bytes_zero1 = (2 + 2) * L.padded_numel + 12 * shard;   // optimizer state partitioned
+  L.bytes_zero2 = 2 * L.padded_numel + (2 + 12) * shard;   // + gradients partitioned
+  L.bytes_zero3 = (2 + 2 + 12) * shard;                    // + parameters partitioned
+  *out = L;
+
+  int32_t count = 0;
+  int64_t t_begin = 0;
+  for (int32_t t = 0; t < n_tensors && t_begin < stop; ++t) {
+    const int64_t t_end = t_begin + numels[t];
+    const int64_t a = t_begin > begin ? t_begin : begin;
+    const int64_t b = t_end < stop ? t_end : stop;
+    if (b > a) {
+      if (count < segs_cap) segs[count] = zero_segment{t, 0, a - t_begin, a - begin, b - a};
+      ++count;
+    }
+    t_begin = t_end;
+  }
+  *n_segs = count;
+  if (count > segs_cap)
+    return fail(ZERO_ERR_CAPACITY, "zero_shard_layout: %d segments needed, capacity %d", count, segs_cap);
+  return ZERO_OK;
+}
+
+int zero_flatten_plan(const zero_segment* segs, int32_t n_segs, const void* const* tensor_ptrs, int32_t n_tensors,
+                      zero_flat_seg* out) {
+  if (n_segs < 0 || (n_segs > 0 && (!segs || !tensor_ptrs || !out)))
+    return fail(ZERO_ERR_INVALID, "zero_flatten_plan: NULL argument");
+  for (int32_t k = 0; k < n_segs; ++k) {
+    const zero_segment& s = segs[k];
+    if (s.tensor < 0 || s.tensor >= n_tensors || !tensor_ptrs[s.tensor] || s.numel <= 0 || s.src_offset < 0 ||
+        s.dst_offset < 0)
+      return fail(ZERO_ERR_INVALID, "zero_flatten_plan: segment %d is invalid", k);
+    out[k] = zero_flat_seg{tensor_ptrs[s.tensor], s.src_offset, s.dst_offset, s.numel};
+  }
+  return ZERO_OK;
+}
+
+int zero_flatten_grads(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype dt, void* shard_dev,
+                       int64_t shard_numel, void* stream) {
+  if (!dtype_ok(dt)) return fail(ZERO_ERR_INVALID, "zero_flatten_grads: unknown dtype %d", static_cast<int>(dt));
+  if (n_segs < 0 || (n_segs > 0 && !segs_dev))
+    return fail(ZERO_ERR_INVALID, "zero_flatten_grads: bad segment table (n_segs=%d)", n_segs);
+  if (shard_numel < 0 || (shard_numel > 0 && !shard_dev))
+    return fail(ZERO_ERR_INVALID, "zero_flatten_grads: bad shard (numel=%lld)", static_cast<long long>(shard_numel));
+  if ((reinterpret_cast<uintptr_t>(shard_dev) & 1u) != 0)
+    return fail(ZERO_ERR_INVALID, "zero_flatten_grads: shard must be 2-byte aligned");
+  if (shard_numel == 0) return ZERO_OK;
+  const int64_t per = flatten_per_block(shard_numel);
+  const int64_t blocks = (shard_numel + per - 1) / per;
+  hipLaunchKernelGGL(flatten_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), segs_dev, n_segs, static_cast<uint16_t*>(shard_dev),
+                     shard_numel, per);
+  return launch_status("zero_flatten_grads");
+}
+
+size_t zero_grad_sqnorm_workspace_bytes(int64_t n) {
+  const int64_t parts = norm_parts(n < 0 ? 0 : n);
+  const size_t bytes = static_cast<size_t>(parts) * (sizeof(double) + sizeof(uint32_t));
+  return (bytes + 255) / 256 * 256;
+}
+
+int zero_grad_sqnorm(const void* shard_dev, zero_dtype dt, int64_t n, void* ws_dev, size_t ws_bytes,
+                     double* sqnorm_dev, int32_t* nonfinite_dev, void* stream) {
+  if (!dtype_ok(dt)) return fail(ZERO_ERR_INVALID, "zero_grad_sqnorm: unknown dtype %d", static_cast<int>(dt));
+  if (n < 0 || (n > 0 && !shard_dev)) return fail(ZERO_ERR_INVALID, "zero_grad_sqnorm: bad shard");
+  if (!sqnorm_dev || !nonfinite_dev || !ws_dev) return fail(ZERO_ERR_INVALID, "zero_grad_sqnorm: NULL output");
+  if (!aligned16(ws_dev)) return fail(ZERO_ERR_INVALID, "zero_grad_sqnorm: workspace must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(shard_dev) & 1u) != 0)
+    return fail(ZERO_ERR_INVALID, "zero_grad_sqnorm: shard must be 2-byte aligned");
+  if (ws_bytes < zero_grad_sqnorm_workspace_bytes(n))
+    return fail(ZERO_ERR_INVALID, "zero_grad_sqnorm: workspace %zu bytes < %zu", ws_bytes,
+                zero_grad_sqnorm_workspace_bytes(n));
+  const int64_t parts = norm_parts(n);
+  const uint16_t* x = static_cast<const uint16_t*>(shard_dev);
+  int64_t head = static_cast<int64_t>(((16u - (reinterpret_cast<uintptr_t>(x) & 15u)) & 15u) >> 1);
+  if (head > n) head = n;
+  const int64_t n8 = (n - head) >> 3;
+  int64_t per = (n8 + parts - 1) / parts;
+  if (per < 1) per = 1;
+  double* part_sum = static_cast<double*>(ws_dev);
+  uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sum + parts);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dt == ZERO_BF16) {
+    hipLaunchKernelGGL(sqnorm_partial_kernel<ZERO_BF16>, dim3(static_cast<unsigned>(parts)), dim3(kBlock), 0, st, x,
+                       n, head, n8, per, part_sum, part_bad);
+  } else {
+    hipLaunchKernelGGL(sqnorm_partial_kernel<ZERO_FP16>, dim3(static_cast<unsigned>(parts)), dim3(kBlock), 0, st, x,
+                       n, head, n8, per, part_sum, part_bad);
+  }
+  int rc = launch_status("zero_grad_sqnorm (partials)");
+  if (rc != ZERO_OK) return rc;
+  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kBlock), 0, st, part_sum, part_bad, parts, sqnorm_dev,
+                     nonfinite_dev);
+  return launch_status("zero_grad_sqnorm (final)");
+}
+
+double zero_clip_coef(double global_sqnorm, double max_norm) {
+  if (!(max_norm > 0.0)) return 1.0;
+  const double coef = max_norm / (std::sqrt(global_sqnorm) + 1e-6);
+  return coef < 1.0 ? coef : 1.0;
+}
+
+int zero_loss_scale_update(double* scale, int32_t nonfinite, int32_t* good_steps, int32_t growth_interval) {
+  if (!scale || !good_steps || growth_interval < 1)
+    return fail(ZERO_ERR_INVALID, "zero_loss_scale_update: bad arguments");
+  if (nonfinite) {
+    *scale *= 0.5;
+    *good_steps = 0;
+    return ZERO_OK;
+  }
+  if (++*good_steps >= growth_interval) {
+    *scale *= 2.0;
+    *good_steps = 0;
+  }
+  return ZERO_OK;
+}
+
+int zero_step_decision(const double* rank_sqnorms, const int32_t* rank_flags, int32_t n_ranks, double max_norm,
+                       double* loss_scale, int32_t* good_steps, int32_t growth_interval, double* grad_scale,
+                       int32_t* skip, double* global_norm) {
+  if (n_ranks < 1 || !rank_sqnorms || !rank_flags || !loss_scale || !good_steps || !grad_scale || !skip ||
+      !global_norm || growth_interval < 1 || !(*loss_scale > 0.0))
+    return fail(ZERO_ERR_INVALID, "zero_step_decision: bad arguments");
+  double global = 0.0;
+  bool overflow = false;
+  for (int32_t r = 0; r < n_ranks; ++r) {  // the all-reduce, in rank order
+    global += rank_sqnorms[r];
+    overflow = overflow || rank_flags[r] != 0;
+  }
+  const double scale = *loss_scale;
+  if (overflow) {
+    *skip = 1;
+    *grad_scale = 0.0;
+    *global_norm = std::numeric_limits<double>::quiet_NaN();
+  } else {
+    const double unscaled = global / (scale * scale);
+    *skip = 0;
+    *grad_scale = zero_clip_coef(unscaled, max_norm) / scale;
+    *global_norm = std::sqrt(unscaled);
+  }
+  return zero_loss_scale_update(loss_scale, overflow ? 1 : 0, good_steps, growth_interval);
+}
+
+double zero_cosine_lr(int64_t t, int64_t total, double lr_max, double lr_min) {
+  if (total <= 1) return lr_max;
+  const double frac = static_cast<double>(t - 1) / static_cast<double>(total - 1);
+  return lr_min + 0.5 * (lr_max - lr_min) * (1.0 + std::cos(M_PI * frac));
+}
+
+int zero_adamw_step(const void* grad_dev, zero_dtype gdt, float* master_dev, float* m_dev, float* v_dev,
+                    uint16_t* param_dev, int64_t n, const zero_adamw_hparams* hp, void* stream) {
+  if (!dtype_ok(gdt)) return fail(ZERO_ERR_INVALID, "zero_adamw_step: unknown dtype %d", static_cast<int>(gdt));
+  if (!hp) return fail(ZERO_ERR_INVALID, "zero_adamw_step: hparams NULL");
+  if (n < 0) return fail(ZERO_ERR_INVALID, "zero_adamw_step: n < 0");
+  if (n > 0 && (!grad_dev || !master_dev || !m_dev || !v_dev || !param_dev))
+    return fail(ZERO_ERR_INVALID, "zero_adamw_step: NULL buffer");
+  if (hp->step < 1 || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) ||
+      !(hp->eps >= 0.0) || !(hp->lr >= 0.0) || !(hp->weight_decay >= 0.0) || !std::isfinite(hp->grad_scale))
+    return fail(ZERO_ERR_INVALID, "zero_adamw_step: hyper-parameters out of range");
+  if (((reinterpret_cast<uintptr_t>(grad_dev) | reinterpret_cast<uintptr_t>(param_dev)) & 1u) != 0 ||
+      ((reinterpret_cast<uintptr_t>(master_dev) | reinterpret_cast<uintptr_t>(m_dev) |
+        reinterpret_cast<uintptr_t>(v_dev)) & 3u) != 0)
+    return fail(ZERO_ERR_INVALID, "zero_adamw_step: buffers not aligned to their element size");
+  if (n == 0) return ZERO_OK;
+
+  const double t = static_cast<double>(hp->step);
+  const double bc1 = 1.0 - std::pow(hp->beta1, t);
+  const double bc2 = 1.0 - std::pow(hp->beta2, t);
+  AdamScalars s;
+  s.b1 = static_cast<float>(hp->beta1);
+  s.omb1 = static_cast<float>(1.0 - hp->beta1);
+  s.b2 = static_cast<float>(hp->beta2);
+  s.omb2 = static_cast<float>(1.0 - hp->beta2);
+  s.eps = static_cast<float>(hp->eps);
+  s.decay = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
+  s.step_size = static_cast<float>(hp->lr / bc1);
+  s.bc2_sqrt = static_cast<float>(std::sqrt(bc2));
+  s.gscale = static_cast<float>(hp->grad_scale);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool vec = aligned16(grad_dev) && aligned16(master_dev) && aligned16(m_dev) && aligned16(v_dev) &&
+                   aligned16(param_dev);
+  const int64_t n8 = vec ? n / 8 : 0;
+  if (n8 > 0) {
+    constexpr int64_t per = kBlock * kAdamUnroll;
+    const int64_t blocks = (n8 + per - 1) / per;
+    if (blocks > std::numeric_limits<int32_t>::max()) return fail(ZERO_ERR_INVALID, "zero_adamw_step: n too large");
+    auto* g = static_cast<const u32x4*>(grad_dev);
+    auto* p = reinterpret_cast<f32x4*>(master_dev);
+    auto* m = reinterpret_cast<f32x4*>(m_dev);
+    auto* v = reinterpret_cast<f32x4*>(v_dev);
+    auto* q = reinterpret_cast<u32x4*>(param_dev);
+    if (gdt == ZERO_BF16) {
+      hipLaunchKernelGGL((adamw_vec_kernel<ZERO_BF16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock),
+                         0, st, g, p, m, v, q, n8, s);
+    } else {
+      hipLaunchKernelGGL((adamw_vec_kernel<ZERO_FP16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock),
+                         0, st, g, p, m, v, q, n8, s);
+    }
+    const int rc = launch_status("zero_adamw_step (vector)");
+    if (rc != ZERO_OK) return rc;
+  }
+  const int64_t done = 8 * n8;
+  const int64_t rest = n - done;
+  if (rest > 0) {
+    int64_t blocks = (rest + kBlock - 1) / kBlock;
+    if (blocks > 65536) blocks = 65536;
+    const uint16_t* g = static_cast<const uint16_t*>(grad_dev) + done;
+    if (gdt == ZERO_BF16) {
+      hipLaunchKernelGGL(adamw_scalar_kernel<ZERO_BF16>, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st, g,
+                         master_dev + done, m_dev + done, v_dev + done, param_dev + done, rest, s);
+    } else {
+      hipLaunchKernelGGL(adamw_scalar_kernel<ZERO_FP16>, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st, g,
+                         master_dev + done, m_dev + done, v_dev + done, param_dev + done, rest, s);
+    }
+    return launch_status("zero_adamw_step (elements)");
+  }
+  return ZERO_OK;
+}
+
+}  // extern "C"

@@ -90,6 +90,9 @@ def _load():
     lib.orc_clip_coef.argtypes = [C.c_double, C.c_double]
     lib.orc_clip_coef.restype = C.c_double
     lib.orc_loss_scale_update.argtypes = [C.POINTER(C.c_double), C.c_int32, C.POINTER(C.c_int32), C.c_int32]
+    lib.orc_step_decision.argtypes = [P, P, C.c_int32, C.c_double, C.POINTER(C.c_double), C.POINTER(C.c_int32),
+                                      C.c_int32, C.POINTER(C.c_double), C.POINTER(C.c_int32),
+                                      C.POINTER(C.c_double)]
     lib.orc_cosine_lr.argtypes = [C.c_int64, C.c_int64, C.c_double, C.c_double]
     lib.orc_cosine_lr.restype = C.c_double
     lib.orc_adamw_scalars.argtypes = [C.POINTER(_HParams), C.POINTER(_Scalars)]
@@ -211,6 +214,23 @@ def loss_scale_update(scale: float, nonfinite: int, good_steps: int, growth_inte
     g = C.c_int32(good_steps)
     _check(lib.orc_loss_scale_update(C.byref(s), nonfinite, C.byref(g), growth_interval), "orc_loss_scale_update")
     return s.value, g.value
+
+
+def step_decision(rank_sqnorms, rank_flags, max_norm: float, loss_scale: float, good_steps: int,
+                  growth_interval: int):
+    """Returns dict(grad_scale, skip, global_norm, loss_scale, good_steps)."""
+    lib = _load()
+    sq = np.ascontiguousarray(np.asarray(rank_sqnorms, dtype=np.float64))
+    fl = np.ascontiguousarray(np.asarray(rank_flags, dtype=np.int32))
+    assert sq.size == fl.size
+    ls = C.c_double(loss_scale)
+    gd = C.c_int32(good_steps)
+    gs = C.c_double(0.0)
+    sk = C.c_int32(0)
+    gn = C.c_double(0.0)
+    _check(lib.orc_step_decision(_ptr(sq), _ptr(fl), sq.size, max_norm, C.byref(ls), C.byref(gd), growth_interval,
+                                 C.byref(gs), C.byref(sk), C.byref(gn)), "orc_step_decision")
+    return dict(grad_scale=gs.value, skip=sk.value, global_norm=gn.value, loss_scale=ls.value, good_steps=gd.value)
 
 
 def cosine_lr(t: int, total: int, lr_max: float, lr_min: float) -> float:

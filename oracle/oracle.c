@@ -224,6 +224,39 @@ int orc_loss_scale_update(double* scale, int32_t nonfinite, int32_t* good_steps,
   return ORC_OK;
 }
 
+/* One rank's host decision after the norm all-reduce, composed from the two
+ * functions above.  The simulated all-reduce sums the ranks' fp64 partial
+ * square-norms in rank order and ORs their flags.  The grads hold g times
+ * the loss scale, so the unscaled square-norm is global / scale²; the update
+ * multiplies each gradient by coef / scale.  Overflow skips the update. */
+int orc_step_decision(const double* rank_sqnorms, const int32_t* rank_flags, int32_t n_ranks, double max_norm,
+                      double* loss_scale, int32_t* good_steps, int32_t growth_interval, double* grad_scale,
+                      int32_t* skip, double* global_norm) {
+  if (n_ranks < 1 || !rank_sqnorms || !rank_flags || !loss_scale || !good_steps || !grad_scale || !skip ||
+      !global_norm || growth_interval < 1 || !(*loss_scale > 0.0)) {
+    return ORC_ERR_INVALID;
+  }
+  double total = 0.0;
+  int32_t flag = 0;
+  for (int32_t r = 0; r < n_ranks; ++r) {
+    total = total + rank_sqnorms[r];
+    if (rank_flags[r]) flag = 1;
+  }
+  double scale = *loss_scale;
+  if (flag) {
+    *skip = 1;
+    *grad_scale = 0.0;
+    *global_norm = NAN;
+  } else {
+    double unscaled = total / (scale * scale);
+    double coef = orc_clip_coef(unscaled, max_norm);
+    *skip = 0;
+    *grad_scale = coef / scale;
+    *global_norm = sqrt(unscaled);
+  }
+  return orc_loss_scale_update(loss_scale, flag, good_steps, growth_interval);
+}
+
 /* Reading for a changing learning rate: half-cosine from lr_max at t=1 down
  * to lr_min at t=total. */
 double orc_cosine_lr(int64_t t, int64_t total, double lr_max, double lr_min) {

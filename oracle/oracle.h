@@ -77,6 +77,9 @@ int orc_sqnorm(const uint16_t* x, int32_t dtype, int64_t n, double* sqnorm, int3
 
 double orc_clip_coef(double global_sqnorm, double max_norm);
 int orc_loss_scale_update(double* scale, int32_t nonfinite, int32_t* good_steps, int32_t growth_interval);
+int orc_step_decision(const double* rank_sqnorms, const int32_t* rank_flags, int32_t n_ranks, double max_norm,
+                      double* loss_scale, int32_t* good_steps, int32_t growth_interval, double* grad_scale,
+                      int32_t* skip, double* global_norm);
 double orc_cosine_lr(int64_t t, int64_t total, double lr_max, double lr_min);
 
 int orc_adamw_scalars(const orc_hparams* hp, orc_scalars* out);

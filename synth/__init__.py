@@ -56,6 +56,8 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build()
+        import torch  # noqa: F401  (PyTorch's HIP runtime first: the fills run on its streams)
+
         lib = C.CDLL(_LIB_PATH)
         lib.syn_fill_host.argtypes = [C.POINTER(Field), C.c_int64, C.c_int64, C.c_void_p, C.c_int32]
         lib.syn_fill_device.argtypes = [C.POINTER(Field), C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]

@@ -1,0 +1,67 @@
+"""Comparison helpers shared by the GPU parity tests (no method arithmetic).
+
+Tolerances (stated by the task this library is held to):
+  * layout, offsets, flatten copies, the non-finite flag: bit-exact;
+  * fp32 master / m / v: |gpu - oracle| <= 1e-6 · |oracle| per element (zeros must match exactly);
+  * bf16 param: within 1 ulp (adjacent bf16 values);
+  * gradient square-norm: within 1e-5 relative of the fp64 oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+REL_STATE = 1e-6
+REL_NORM = 1e-5
+
+
+def assert_bits_equal(got: np.ndarray, ref: np.ndarray, what: str) -> None:
+    got = np.ascontiguousarray(got).reshape(-1)
+    ref = np.ascontiguousarray(ref).reshape(-1)
+    k = got.dtype.itemsize
+    assert ref.dtype.itemsize == k and got.size == ref.size, (what, got.dtype, ref.dtype, got.size, ref.size)
+    diff = np.nonzero((got.view(np.uint8).reshape(-1, k) != ref.view(np.uint8).reshape(-1, k)).any(axis=1))[0]
+    if diff.size:
+        raise AssertionError(f"{what}: {diff.size} of {got.size} elements differ, first at {diff[:5]}: "
+                             f"got {got[diff[:5]]} want {ref[diff[:5]]}")
+
+
+def assert_f32_close(got: np.ndarray, ref: np.ndarray, what: str, rel: float = REL_STATE) -> int:
+    """Returns the number of elements whose bits differ (0 expected)."""
+    got = np.asarray(got, dtype=np.float32)
+    ref = np.asarray(ref, dtype=np.float32)
+    assert got.shape == ref.shape
+    same = got.view(np.uint32) == ref.view(np.uint32)
+    g64, r64 = got.astype(np.float64), ref.astype(np.float64)
+    ok = same | (np.abs(g64 - r64) <= rel * np.abs(r64))
+    if not ok.all():
+        idx = np.nonzero(~ok)[0][:5]
+        raise AssertionError(f"{what}: {int((~ok).sum())} elements beyond {rel} relative, e.g. idx {idx}: "
+                             f"got {got[idx]} want {ref[idx]}")
+    return int((~same).sum())
+
+
+def assert_bf16_within_ulp(got: np.ndarray, ref: np.ndarray, what: str, ulps: int = 1) -> int:
+    """bf16 bit patterns (uint16). Compares positions on the ordered number line."""
+    def ordered(x):
+        x = x.astype(np.int32)
+        return np.where(x & 0x8000, -(x & 0x7FFF), x)
+    got = np.asarray(got, dtype=np.uint16)
+    ref = np.asarray(ref, dtype=np.uint16)
+    d = np.abs(ordered(got) - ordered(ref))
+    if (d > ulps).any():
+        idx = np.nonzero(d > ulps)[0][:5]
+        raise AssertionError(f"{what}: {int((d > ulps).sum())} params beyond {ulps} ulp, e.g. {idx}: "
+                             f"got {got[idx]} want {ref[idx]}")
+    return int((d != 0).sum())
+
+
+def assert_norm_close(got: float, ref: float, n: int, what: str) -> None:
+    assert np.isfinite(got) and np.isfinite(ref), (what, got, ref)
+    if ref == 0.0:
+        assert got == 0.0, (what, got)
+        return
+    rel = abs(got - ref) / abs(ref)
+    assert rel <= REL_NORM, f"{what}: relative error {rel:.3e} > {REL_NORM}"
+    # Any summation order of n non-negative fp64 terms stays within n·2^-53 of the exact sum, and so does
+    # the sequential oracle: the two can differ by at most twice that.
+    assert rel <= 2 * max(n, 1) * 2.0**-53, f"{what}: relative error {rel:.3e} beyond fp64 summation bound"

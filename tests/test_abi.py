@@ -1,0 +1,147 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, rejects bad arguments before touching the device, and its host-only
+entry points (layout, decision helpers) match the oracle exactly."""
+import math
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import mixed_precision_adam_amd as Z
+import oracle
+from synth.workloads import WORKLOADS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "zero_shard.h")
+
+
+def _declared():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 11
+    lib = Z.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(Z.EXPORTS)
+
+
+def test_invalid_arguments_rejected_without_device():
+    lib = Z.library()
+    assert lib.zero_adamw_step(None, 0, None, None, None, None, -1, None, None) == Z.ZERO_ERR_INVALID
+    hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 0)  # step 0 is invalid
+    rc = lib.zero_adamw_step(16, 0, 16, 16, 16, 16, 8, hp, None)
+    assert rc == Z.ZERO_ERR_INVALID and "hyper" in Z.zero_last_error()
+    hp = Z.zero_adamw_hparams(1e-3, 1.0, 0.999, 1e-8, 0.0, 1.0, 1)  # beta1 = 1 is invalid
+    assert lib.zero_adamw_step(16, 0, 16, 16, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID
+    hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, float("inf"), 1)
+    assert lib.zero_adamw_step(16, 0, 16, 16, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID
+    hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 1)
+    assert lib.zero_adamw_step(16, 7, 16, 16, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID  # dtype
+    assert lib.zero_adamw_step(16, 0, 18, 16, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID  # fp32 misaligned
+    assert lib.zero_adamw_step(None, 0, 16, 16, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_adamw_step(None, 0, None, None, None, None, 0, hp, None) == Z.ZERO_OK  # n = 0: no-op
+    assert lib.zero_flatten_grads(None, 3, 0, 16, 8, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_flatten_grads(16, -1, 0, 16, 8, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_flatten_grads(16, 1, 0, 17, 8, None) == Z.ZERO_ERR_INVALID  # odd shard address
+    assert lib.zero_flatten_grads(16, 1, 0, None, 8, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_flatten_grads(None, 0, 0, None, 0, None) == Z.ZERO_OK
+    ws = Z.zero_grad_sqnorm_workspace_bytes(1000)
+    assert ws % 256 == 0 and ws >= 12
+    assert lib.zero_grad_sqnorm(16, 0, 1000, 256, ws - 1, 16, 16, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_grad_sqnorm(16, 0, 1000, 257, ws, 16, 16, None) == Z.ZERO_ERR_INVALID  # ws alignment
+    assert lib.zero_grad_sqnorm(16, 0, 1000, 256, ws, None, 16, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_grad_sqnorm(None, 0, 10, 256, ws, 16, 16, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_grad_sqnorm(16, 2, 10, 256, ws, 16, 16, None) == Z.ZERO_ERR_INVALID
+
+
+def test_workspace_size_is_bounded():
+    assert Z.zero_grad_sqnorm_workspace_bytes(0) == 256
+    assert Z.zero_grad_sqnorm_workspace_bytes(10**12) <= 64 * 1024
+
+
+def _same_layout(numels, world, rank):
+    lay, segs = Z.zero_shard_layout(numels, world, rank)
+    ref = oracle.layout(numels, world, rank)
+    for f in ("psi", "padded_numel", "shard_numel", "shard_offset", "shard_valid", "world", "rank", "bytes_dp",
+              "bytes_zero1", "bytes_zero2", "bytes_zero3"):
+        assert getattr(lay, f) == getattr(ref, f), (f, numels, world, rank)
+    assert [(s.tensor, s.src_offset, s.dst_offset, s.numel) for s in segs] == ref.segments
+
+
+def test_layout_parity_brute_force():
+    rng = random.Random(99)
+    for psi in range(0, 70):
+        for world in range(1, 10):
+            cuts = sorted(rng.randint(0, psi) for _ in range(rng.randint(0, 6)))
+            numels = [b - a for a, b in zip([0] + cuts, cuts + [psi])]
+            for rank in range(world):
+                _same_layout(numels, world, rank)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_layout_parity_workloads(name):
+    w = WORKLOADS[name]
+    for rank in sorted(set(w.ranks + [0, w.world - 1, w.world // 2])):
+        _same_layout(w.numels, w.world, rank)
+
+
+def test_layout_errors_and_capacity():
+    lib = Z.library()
+    arr = (Z.C.c_int64 * 8)(*([1] * 8))
+    out = Z.zero_layout()
+    n = Z.C.c_int32(-1)
+    segs = (Z.zero_segment * 3)()
+    assert lib.zero_shard_layout(Z.C.cast(arr, Z._P), 8, 1, 0, Z.C.byref(out), Z.C.cast(segs, Z._P), 3,
+                                 Z.C.byref(n)) == Z.ZERO_ERR_CAPACITY
+    assert n.value == 8 and out.psi == 8
+    assert lib.zero_shard_layout(Z.C.cast(arr, Z._P), 8, 0, 0, Z.C.byref(out), None, 0, Z.C.byref(n)) == -1
+    assert lib.zero_shard_layout(Z.C.cast(arr, Z._P), 8, 4, 4, Z.C.byref(out), None, 0, Z.C.byref(n)) == -1
+    bad = (Z.C.c_int64 * 1)(-5)
+    assert lib.zero_shard_layout(Z.C.cast(bad, Z._P), 1, 4, 0, Z.C.byref(out), None, 0, Z.C.byref(n)) == -1
+    huge = (Z.C.c_int64 * 2)(2**62, 2**62)
+    assert lib.zero_shard_layout(Z.C.cast(huge, Z._P), 2, 4, 0, Z.C.byref(out), None, 0, Z.C.byref(n)) == -1
+
+
+def test_host_decision_parity():
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        k = int(rng.integers(1, 9))
+        sq = list(rng.random(k) * 10 ** rng.uniform(-6, 6))
+        fl = [int(x) for x in (rng.random(k) < 0.1)]
+        args = (float(rng.choice([0.0, 0.5, 1.0, 5.0])), float(2.0 ** rng.integers(0, 17)), int(rng.integers(0, 5)),
+                int(rng.integers(1, 6)))
+        a = Z.zero_step_decision(sq, fl, *args)
+        b = oracle.step_decision(sq, fl, *args)
+        for key in ("grad_scale", "skip", "loss_scale", "good_steps"):
+            assert a[key] == b[key], (key, a, b)
+        assert (math.isnan(a["global_norm"]) and math.isnan(b["global_norm"])) or a["global_norm"] == b["global_norm"]
+    for t in range(1, 11):
+        assert Z.zero_cosine_lr(t, 10, 1e-4, 1e-5) == oracle.cosine_lr(t, 10, 1e-4, 1e-5)
+    for sq, mx in [(0.0, 1.0), (1.0, 1.0), (1e6, 1.0), (3.0, 0.0), (4.0, -1.0)]:
+        assert Z.zero_clip_coef(sq, mx) == oracle.clip_coef(sq, mx)
+    for flag in (0, 1):
+        assert Z.zero_loss_scale_update(1024.0, flag, 2, 3) == oracle.loss_scale_update(1024.0, flag, 2, 3)
+
+
+def test_flatten_plan_packs_descriptors():
+    lay, segs = Z.zero_shard_layout([10, 20, 30], 2, 0)  # rank 0 owns flat [0, 30)
+    blob = Z.zero_flatten_plan(segs, [0x1000, 0x2000, 0])  # tensor 2 does not land: no address needed
+    rec = np.frombuffer(blob, dtype=np.int64).reshape(-1, 4)
+    assert rec.shape == (2, 4)
+    assert tuple(rec[0]) == (0x1000, 0, 0, 10) and tuple(rec[1]) == (0x2000, 0, 10, 20)
+    with pytest.raises(Z.ZeroError):
+        Z.zero_flatten_plan(segs, [0x1000, 0, 0x3000])  # a landing tensor without an address
+
+
+def test_single_hip_runtime():
+    import synth
+
+    synth._load()
+    paths = Z.hip_runtimes_loaded()
+    assert len(paths) == 1 and "torch" in paths[0], paths

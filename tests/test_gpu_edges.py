@@ -1,0 +1,244 @@
+"""GPU parity on small and ragged cases: each C-ABI call against the oracle.
+
+Cases span several tiles plus ragged tails, unaligned base addresses (scalar
+paths), empty inputs, all-padding shards and non-finite gradients.  Every
+operand sits inside a guard region whose sentinel bits must survive the call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.parity import assert_bf16_within_ulp, assert_bits_equal, assert_f32_close, assert_norm_close
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import mixed_precision_adam_amd as Z
+
+DEV = "cuda:0"
+GUARD = 64  # elements of sentinel on each side
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def guarded(n: int, dtype, offset: int = 0, fill=None):
+    """A tensor of n elements starting `offset` elements past a 256-byte aligned base, plus its guard buffer."""
+    total = GUARD + offset + n + GUARD
+    buf = torch.empty(total, dtype=dtype, device=DEV)
+    if dtype in (torch.float32,):
+        buf.view(torch.int32).fill_(0x7FA5A5A5)
+    else:
+        buf.view(torch.int16).fill_(0x5A5A)
+    view = buf[GUARD + offset: GUARD + offset + n]
+    if fill is not None:
+        view.copy_(fill)
+    return buf, view
+
+
+def check_guards(buf: torch.Tensor, offset: int, n: int, what: str):
+    if buf.dtype == torch.float32:
+        raw = buf.view(torch.int32).cpu().numpy()
+        sentinel = 0x7FA5A5A5
+    else:
+        raw = buf.view(torch.int16).cpu().numpy().view(np.uint16)
+        sentinel = 0x5A5A
+    lo = GUARD + offset
+    assert (raw[:lo] == sentinel).all() and (raw[lo + n:] == sentinel).all(), f"{what}: guard overwritten"
+
+
+def to_dev16(bits: np.ndarray, dtype) -> torch.Tensor:
+    return torch.from_numpy(bits.view(np.int16).copy()).to(DEV).view(dtype)
+
+
+# ----------------------------------------------------------------------------- flatten
+
+def _flatten_case(numels, world, src_offsets, dt, seed):
+    rng = np.random.default_rng(seed)
+    tdt = torch.bfloat16 if dt == 0 else torch.float16
+    host = [rng.integers(0, 65536, n, dtype=np.uint32).astype(np.uint16) for n in numels]
+    keep, srcs = [], []
+    for h, off in zip(host, src_offsets):
+        buf, view = guarded(len(h), tdt, off)
+        view.copy_(to_dev16(h, tdt)) if len(h) else None
+        keep.append(buf)
+        srcs.append(view.data_ptr() if len(h) else 0)
+    for rank in range(world):
+        lay, segs = Z.zero_shard_layout(numels, world, rank)
+        s = lay.shard_numel
+        table = Z.zero_flatten_plan(segs, srcs)
+        tab = torch.frombuffer(bytearray(table or b"\0" * 32), dtype=torch.uint8).to(DEV)
+        for dst_off in (0, 3):
+            sbuf, shard = guarded(s, tdt, dst_off)
+            Z.zero_flatten_grads(tab, len(segs), dt, shard, s)
+            torch.cuda.synchronize()
+            ref = oracle.flatten(host, numels, world, rank)
+            assert_bits_equal(bits16(shard), ref, f"flatten rank {rank}/{world} dst_off {dst_off}")
+            check_guards(sbuf, dst_off, s, "flatten shard")
+    for buf, off, h in zip(keep, src_offsets, host):
+        check_guards(buf, off, len(h), "flatten source")
+
+
+@pytest.mark.parametrize("dt", [0, 1])
+def test_flatten_ragged_lists(dt):
+    _flatten_case([1000, 1, 0, 77, 4096, 5, 30011], 4, [0] * 7, dt, 1)
+    _flatten_case([1000, 1, 0, 77, 4096, 5, 30011], 3, [1, 0, 0, 3, 5, 7, 2], dt, 2)  # mismatched phases
+    _flatten_case([8] * 50 + [123457], 8, [8] * 51, dt, 3)
+
+
+def test_flatten_many_blocks_and_padding():
+    # > 1 workgroup per piece, shard not a multiple of 8, last rank mostly padding
+    _flatten_case([200_003, 65_536 * 5 + 3, 17], 7, [0, 8, 1], 0, 4)
+
+
+def test_flatten_all_padding_ranks():
+    _flatten_case([5], 9, [0], 0, 5)  # ranks 5..8 own only padding
+    _flatten_case([1], 1, [0], 1, 6)
+
+
+# ----------------------------------------------------------------------------- square-norm
+
+def _gpu_sqnorm(bits: np.ndarray, dt: int, offset: int):
+    tdt = torch.bfloat16 if dt == 0 else torch.float16
+    n = bits.size
+    buf, x = guarded(n, tdt, offset)
+    if n:
+        x.copy_(to_dev16(bits, tdt))
+    wsb = Z.zero_grad_sqnorm_workspace_bytes(n)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    out = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+    flag = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    Z.zero_grad_sqnorm(x, dt, n, ws, wsb, out, flag)
+    torch.cuda.synchronize()
+    check_guards(buf, offset, n, "sqnorm input")
+    return float(out.cpu()[0]), int(flag.cpu()[0])
+
+
+@pytest.mark.parametrize("dt", [0, 1])
+@pytest.mark.parametrize("n", [0, 1, 7, 8, 9, 255, 4097, 65_536 * 3 + 5, 1_000_003])
+def test_sqnorm_sizes(dt, n):
+    rng = np.random.default_rng(n + 10 * dt)
+    if dt == 0:
+        bits = oracle.f32_to_bf16((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    else:  # fp16 with a loss-scale-like magnitude plus some subnormals
+        v = rng.standard_normal(n) * 60.0
+        v[::97] = 3e-7
+        bits = v.astype(np.float16).view(np.uint16)
+    ref, rflag = oracle.sqnorm(bits, dt)
+    for offset in (0, 1, 5):
+        got, flag = _gpu_sqnorm(bits, dt, offset)
+        assert flag == rflag == 0
+        assert_norm_close(got, ref, n, f"sqnorm n={n} off={offset}")
+
+
+def test_sqnorm_is_deterministic():
+    rng = np.random.default_rng(0)
+    bits = oracle.f32_to_bf16((rng.standard_normal(3_000_001) * 1e-3).astype(np.float32))
+    a = _gpu_sqnorm(bits, 0, 0)
+    b = _gpu_sqnorm(bits, 0, 0)
+    assert a == b
+
+
+@pytest.mark.parametrize("dt,pattern", [(0, 0x7F80), (0, 0xFF80), (0, 0x7FC1), (1, 0x7C00), (1, 0xFC00), (1, 0x7E00)])
+@pytest.mark.parametrize("where", [0, 3, 77_777, 199_999])
+def test_sqnorm_nonfinite(dt, pattern, where):
+    bits = np.zeros(200_000, dtype=np.uint16)
+    bits[where] = pattern
+    for offset in (0, 3):
+        _, flag = _gpu_sqnorm(bits, dt, offset)
+        assert flag == 1
+
+
+def test_sqnorm_max_finite_is_not_flagged():
+    bits = np.full(1000, 0x7F7F, dtype=np.uint16)
+    got, flag = _gpu_sqnorm(bits, 0, 0)
+    ref, _ = oracle.sqnorm(bits, 0)
+    assert flag == 0
+    assert_norm_close(got, ref, 1000, "max bf16")
+
+
+# ----------------------------------------------------------------------------- AdamW
+
+HP_SETS = [
+    dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01),
+    dict(lr=1e-2, beta1=0.8, beta2=0.95, eps=1e-3, weight_decay=0.1),
+    dict(lr=0.0, beta1=0.0, beta2=0.0, eps=1e-6, weight_decay=0.5),
+]
+
+
+def _adam_case(n, dt, offset, hp, steps, seed, gscales=(1.0, 0.3, 2.0)):
+    rng = np.random.default_rng(seed)
+    tdt = torch.bfloat16 if dt == 0 else torch.float16
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    p0[::31] = 0.0
+    bufs = {k: guarded(n, torch.float32, offset) for k in ("p", "m", "v")}
+    bufs["p"][1].copy_(torch.from_numpy(p0))
+    bufs["m"][1].zero_()
+    bufs["v"][1].zero_()
+    qbuf, q = guarded(n, torch.bfloat16, offset)
+    gbuf, g = guarded(n, tdt, offset)
+    rp, rm, rv = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    rq = np.zeros(n, np.uint16)
+    for t in range(1, steps + 1):
+        if dt == 0:
+            gb = oracle.f32_to_bf16((rng.standard_normal(n) * 1e-3).astype(np.float32))
+        else:
+            v = rng.standard_normal(n) * 60.0
+            v[::53] = 1e-7  # subnormal fp16
+            gb = v.astype(np.float16).view(np.uint16)
+        gb[::29] = 0
+        if n:
+            g.copy_(to_dev16(gb, tdt))
+        gs = gscales[(t - 1) % len(gscales)]
+        Z.zero_adamw_step(g, dt, bufs["p"][1], bufs["m"][1], bufs["v"][1], q, n, grad_scale=gs, step=t, **hp)
+        oracle.adamw_step(gb, dt, rp, rm, rv, rq, grad_scale=gs, step=t, **hp)
+        torch.cuda.synchronize()
+        what = f"adamw n={n} dt={dt} off={offset} t={t}"
+        nd = assert_f32_close(bufs["p"][1].cpu().numpy(), rp, what + " master")
+        nd += assert_f32_close(bufs["m"][1].cpu().numpy(), rm, what + " m")
+        nd += assert_f32_close(bufs["v"][1].cpu().numpy(), rv, what + " v")
+        nd += assert_bf16_within_ulp(bits16(q), rq, what + " param")
+        assert nd == 0, f"{what}: {nd} elements not bit-identical (within tolerance)"
+    for k, (buf, _) in bufs.items():
+        check_guards(buf, offset, n, "adamw " + k)
+    check_guards(qbuf, offset, n, "adamw param")
+    check_guards(gbuf, offset, n, "adamw grad")
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 15, 16, 17, 4096 + 8 + 3, 100_003])
+@pytest.mark.parametrize("dt", [0, 1])
+def test_adamw_sizes_aligned(n, dt):
+    _adam_case(n, dt, 0, HP_SETS[0], 3, n + dt)
+
+
+@pytest.mark.parametrize("offset", [1, 4, 8])
+def test_adamw_offsets(offset):
+    _adam_case(10_007, 0, offset, HP_SETS[1], 2, offset)
+
+
+@pytest.mark.parametrize("hi", range(len(HP_SETS)))
+def test_adamw_hparam_sets(hi):
+    _adam_case(65_536 + 13, 0, 0, HP_SETS[hi], 3, 100 + hi)
+    _adam_case(65_536 + 13, 1, 0, HP_SETS[hi], 2, 200 + hi, gscales=(2.0**-16, 2.0**-15))
+
+
+def test_adamw_zero_padding_stays_zero():
+    n = 4099
+    p = torch.zeros(n, device=DEV)
+    m = torch.zeros(n, device=DEV)
+    v = torch.zeros(n, device=DEV)
+    q = torch.full((n,), 1.0, dtype=torch.bfloat16, device=DEV)
+    g = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    for t in (1, 2):
+        Z.zero_adamw_step(g, 0, p, m, v, q, n, grad_scale=0.5, step=t, **HP_SETS[1])
+    torch.cuda.synchronize()
+    for x in (p, m, v):
+        assert (x.view(torch.int32) == 0).all()
+    assert (q.view(torch.int16) == 0).all()
+
+
+def test_adamw_empty_is_noop():
+    Z.zero_adamw_step(0, 0, 0, 0, 0, 0, 0, grad_scale=1.0, step=1, **HP_SETS[0])

@@ -141,3 +141,30 @@ def test_cosine_lr_against_torch_closed_form():
         sched.step()
     assert oracle.cosine_lr(1, total, lr_max, lr_min) == lr_max
     assert math.isclose(oracle.cosine_lr(total, total, lr_max, lr_min), lr_min, rel_tol=1e-15)
+
+
+def test_step_decision_against_torch_unscale_and_clip():
+    """Unscaling by the loss scale then clip_grad_norm_ (torch, CPU fp64) on the gradients of several
+    simulated ranks gives the same per-element multiplier as the oracle's decision."""
+    rng = np.random.default_rng(17)
+    scale = 1024.0
+    ranks = [rng.standard_normal(1000) * 1e-2 * scale for _ in range(4)]
+    sq = [float(np.dot(g, g)) for g in ranks]
+    dec = oracle.step_decision(sq, [0] * 4, 1.0, scale, 0, 1000)
+    params = []
+    for g in ranks:
+        p = torch.nn.Parameter(torch.zeros(1000, dtype=torch.float64))
+        p.grad = torch.from_numpy(g / scale)
+        params.append(p)
+    total = torch.nn.utils.clip_grad_norm_(params, 1.0, foreach=False)
+    assert dec["skip"] == 0 and math.isclose(dec["global_norm"], float(total), rel_tol=1e-13)
+    for g, p in zip(ranks, params):
+        np.testing.assert_allclose(g * dec["grad_scale"], p.grad.numpy(), rtol=1e-13)
+    assert dec["loss_scale"] == scale and dec["good_steps"] == 1
+
+
+def test_step_decision_overflow_skips_and_halves():
+    dec = oracle.step_decision([1.0, float("inf"), 2.0], [0, 1, 0], 1.0, 65536.0, 7, 1000)
+    assert dec["skip"] == 1 and dec["loss_scale"] == 32768.0 and dec["good_steps"] == 0
+    dec = oracle.step_decision([4.0], [0], 0.0, 1.0, 0, 2**31 - 1)
+    assert dec["skip"] == 0 and dec["grad_scale"] == 1.0 and dec["global_norm"] == 2.0
