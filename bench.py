@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark: one data-parallel rank's ZeRO step on one MI355X.
+
+A step is the whole hot path on one rank's shard: shard layout (host),
+flatten of the per-tensor bf16 gradients into the rank's contiguous shard,
+fp64 gradient square-norm with the non-finite flag, the host decision (clip
+coefficient, loss scale, skip) after reading the 12-byte result, and the fused
+AdamW update of the fp32 master/m/v shard with the bf16 parameter writeback.
+
+Default workload: GPT-2 1.5B tensor list (48 layers, d=1600, ffn 6400, vocab
+50257, ctx 1024), N = 8 data-parallel ranks, rank 0's shard of 194,701,400
+parameters, synthetic bf16 gradients ~N(0, 1e-3) already resident in HBM.
+
+Prints one JSON line.  Per-kernel durations come from HIP events recorded on
+the stream the kernels run on; the roofline entry is for the fused AdamW
+kernel (28 algorithmic bytes per parameter: read grad 2 + master/m/v 12,
+write master/m/v 12 + param 2).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "params updated/sec and HBM GB/s (% of peak) for sharded fused AdamW step, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+ADAM_BYTES_PER_PARAM = 28
+FLATTEN_BYTES_PER_PARAM = 4
+NORM_BYTES_PER_PARAM = 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2-1.5b")
+    ap.add_argument("--state", choices=("tiled", "arrays"), default="tiled",
+                    help="optimizer-state layout: tiled master/m/v (default) or three separate arrays")
+    ap.add_argument("--unfused", action="store_true", help="flatten and square-norm as two passes")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="elements of the shard the oracle times (0: all)")
+    ap.add_argument("--cpu-steps", type=int, default=3, help="steps the oracle times")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="only run plain device copies of this many bytes (for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def copy_calibration(nbytes: int, reps: int = 10) -> None:
+    import torch
+
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+def cpu_baseline(w, sample: int, steps: int) -> dict:
+    """The oracle (single-threaded C), untuned, on the first `sample` elements of the rank's shard:
+    `steps` whole steps (flatten + square-norm + decision + AdamW), timed with a monotonic clock."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    rank = w.ranks[0]
+    lay = oracle.layout(w.numels, w.world, rank)
+    sample = min(sample, lay.shard_valid) if sample > 0 else lay.shard_valid
+    lo, hi = lay.shard_offset, lay.shard_offset + sample
+    numels, tensors = [], []
+    start = 0
+    gf = w.grad_field(1)
+    for n in w.numels:  # the tensors' parts that fall in the sample, as their own tensor list
+        a, b = max(start, lo), min(start + n, hi)
+        if b > a:
+            numels.append(b - a)
+            tensors.append(synth.fill_host(gf, a, b - a))
+        start += n
+    master = synth.fill_host(w.master_field(), lo, sample)
+    m = np.zeros(sample, np.float32)
+    v = np.zeros(sample, np.float32)
+    q = np.zeros(sample, np.uint16)
+    t0 = time.perf_counter()
+    for t in range(1, steps + 1):
+        shard = oracle.flatten(tensors, numels, 1, 0)
+        sq, flag = oracle.sqnorm(shard, oracle.BF16)
+        dec = oracle.step_decision([sq], [flag], w.clip, 1.0, 0, 2**31 - 1)
+        oracle.adamw_step(shard, oracle.BF16, master, m, v, q, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                          weight_decay=w.weight_decay, grad_scale=dec["grad_scale"], step=t)
+    dt = time.perf_counter() - t0
+    return {"value": sample * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{'whole' if sample == lay.shard_valid else f'first {sample} params of the'} rank's shard "
+                      f"({sample} params, {len(numels)} tensor pieces), {steps} full steps (flatten + fp64 sqnorm "
+                      f"+ decision + AdamW) on the same gradients, {dt:.2f} s on one host core"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import torch
+
+    import mixed_precision_adam_amd as Z
+    import synth
+    from mixed_precision_adam_amd.driver import AdamWConfig, RankShard, ScalerState
+    from synth.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    assert not w.flat_shard_only, "bench workloads flatten per-tensor gradients"
+    dev = torch.device("cuda:0")
+    rank = w.ranks[0]
+    torch.cuda.set_device(dev)
+
+    # --- inputs resident in HBM: the rank's landing tensors, master init, zero m/v
+    lay, segs = Z.zero_shard_layout(w.numels, w.world, rank)
+    starts = [0]
+    for n in w.numels:
+        starts.append(starts[-1] + n)
+    landing = sorted({s.tensor for s in segs})
+    dt16 = torch.bfloat16 if w.grad_kind == synth.BF16 else torch.float16
+    sources = [None] * len(w.numels)
+    gf = w.grad_field(1)
+    for t in landing:
+        sources[t] = torch.empty(w.numels[t], dtype=dt16, device=dev)
+        synth.fill_tensor(gf, starts[t], sources[t])
+    gdt = Z.ZERO_BF16 if w.grad_kind == synth.BF16 else Z.ZERO_FP16
+    sh = RankShard(w.numels, w.world, rank, gdt, dev, sources=sources, tiled=args.state == "tiled",
+                   fused=not args.unfused)
+    master0 = torch.zeros(lay.shard_numel, dtype=torch.float32, device=dev)
+    synth.fill_tensor(w.master_field(), lay.shard_offset, master0[:lay.shard_valid])
+    sh.load_master(master0)
+    del master0
+    cfg = AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+                      max_norm=w.clip)
+    scaler = ScalerState(scale=w.loss_scale, growth_interval=2**31 - 1 if w.grad_kind == synth.BF16 else 1000)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    ev = {k: [] for k in ("flatten", "sqnorm", "adamw")}
+
+    def step(record: bool):
+        # a1: layout (host) -- recomputed every step as part of the path
+        Z.zero_shard_layout(w.numels, w.world, rank)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if record else None
+        if record:
+            e[0].record(stream)
+        sh.flatten()                                   # a2 (+ a3 when fused)
+        if record:
+            e[1].record(stream)
+            e[2].record(stream)
+        if not sh.fused:
+            sh.sqnorm()                                # a3
+        if record:
+            e[3].record(stream)
+        sh.readback()                                  # 12 bytes to the host
+        stream.synchronize()
+        sq, fl = sh.norm_result()                      # a4: host decision
+        dec = Z.zero_step_decision([sq], [fl], cfg.max_norm, scaler.scale, scaler.good_steps,
+                                   scaler.growth_interval)
+        scaler.scale, scaler.good_steps = dec["loss_scale"], dec["good_steps"]
+        if not dec["skip"]:
+            scaler.adam_step += 1
+            if record:
+                e[4].record(stream)
+            sh.adamw(cfg, dec["grad_scale"], scaler.adam_step)   # a5
+            if record:
+                e[5].record(stream)
+        if record:
+            ev["flatten"].append((e[0], e[1]))
+            ev["sqnorm"].append((e[2], e[3]))
+            if not dec["skip"]:
+                ev["adamw"].append((e[4], e[5]))
+        return dec
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, synchronized on both sides (one process: no barrier needed)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dec = step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    def avg_ms(pairs):
+        return sum(a.elapsed_time(b) for a, b in pairs) / max(len(pairs), 1)
+
+    S = lay.shard_numel
+    ms = {k: avg_ms(v) for k, v in ev.items()}
+    adam_gbs = ADAM_BYTES_PER_PARAM * S / (ms["adamw"] * 1e-3) / 1e9
+    ms_per_step = elapsed / args.steps * 1e3
+    params_per_s = S * args.steps / elapsed
+    step_bpp = ADAM_BYTES_PER_PARAM + FLATTEN_BYTES_PER_PARAM + (0 if sh.fused else NORM_BYTES_PER_PARAM)
+    result = {
+        "metric": METRIC,
+        "value": params_per_s,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: rank {rank} of N={w.world}, shard {S} params "
+                        f"(psi={lay.psi}, {len(segs)} tensor pieces), {'bf16' if gdt == 0 else 'fp16'} grads",
+            "psi": lay.psi, "world": w.world, "rank": rank, "shard_numel": S, "segments": len(segs),
+        },
+        "roofline": {
+            "kernel": "adamw_tiled_kernel" if sh.tiled else "adamw_vec_kernel",
+            "bound": "hbm",
+            "achieved": adam_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": adam_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_param": ADAM_BYTES_PER_PARAM,
+        },
+        "breakdown": {
+            "adamw_ms": ms["adamw"],
+            "adamw_params_per_s": S / (ms["adamw"] * 1e-3),
+            "state_layout": args.state,
+            "flatten_norm_fused": sh.fused,
+            "flatten_ms": ms["flatten"],
+            "flatten_gbs": FLATTEN_BYTES_PER_PARAM * S / (ms["flatten"] * 1e-3) / 1e9,
+            "sqnorm_ms": ms["sqnorm"],
+            "sqnorm_gbs": (NORM_BYTES_PER_PARAM * S / (ms["sqnorm"] * 1e-3) / 1e9) if not sh.fused else None,
+            "step_bytes_per_param": step_bpp,
+            "step_gbs_algorithmic": step_bpp * params_per_s / 1e9,
+            "last_global_norm": dec["global_norm"],
+            "last_grad_scale": dec["grad_scale"],
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample, args.cpu_steps)
+        result["cpu_baseline"]["host_cores_available"] = os.cpu_count()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -85,11 +85,20 @@ _lib.zero_loss_scale_update.argtypes = [C.POINTER(C.c_double), C.c_int32, C.POIN
 _lib.zero_cosine_lr.argtypes = [C.c_int64, C.c_int64, C.c_double, C.c_double]
 _lib.zero_cosine_lr.restype = C.c_double
 _lib.zero_adamw_step.argtypes = [_P, C.c_int, _P, _P, _P, _P, C.c_int64, C.POINTER(zero_adamw_hparams), _P]
+_lib.zero_flatten_grads_sqnorm.argtypes = [_P, C.c_int32, C.c_int, _P, C.c_int64, _P, C.c_size_t, _P, _P, _P]
+_lib.zero_state_tiled_numel.argtypes = [C.c_int64]
+_lib.zero_state_tiled_numel.restype = C.c_int64
+_lib.zero_adamw_step_tiled.argtypes = [_P, C.c_int, _P, _P, C.c_int64, C.POINTER(zero_adamw_hparams), _P]
+_lib.zero_state_tile.argtypes = [_P, _P, _P, _P, C.c_int64, _P]
+_lib.zero_state_untile.argtypes = [_P, _P, _P, _P, C.c_int64, _P]
+
+ZERO_STATE_TILE = 1024
 
 # Every symbol include/zero_shard.h declares.
 EXPORTS = ("zero_last_error", "zero_shard_layout", "zero_flatten_plan", "zero_flatten_grads",
-           "zero_grad_sqnorm_workspace_bytes", "zero_grad_sqnorm", "zero_step_decision", "zero_clip_coef",
-           "zero_loss_scale_update", "zero_cosine_lr", "zero_adamw_step")
+           "zero_flatten_grads_sqnorm", "zero_grad_sqnorm_workspace_bytes", "zero_grad_sqnorm", "zero_step_decision",
+           "zero_clip_coef", "zero_loss_scale_update", "zero_cosine_lr", "zero_adamw_step", "zero_state_tiled_numel",
+           "zero_adamw_step_tiled", "zero_state_tile", "zero_state_untile")
 
 
 def library() -> C.CDLL:
@@ -207,3 +216,28 @@ def zero_adamw_step(grad, dtype: int, master, m, v, param, n: int, *, lr: float,
     hp = zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, grad_scale, step)
     _check(_lib.zero_adamw_step(_addr(grad), dtype, _addr(master), _addr(m), _addr(v), _addr(param), n,
                                 C.byref(hp), _stream(stream)))
+
+
+def zero_flatten_grads_sqnorm(segs_dev, n_segs: int, dtype: int, shard, shard_numel: int, ws, ws_bytes: int,
+                              sqnorm_out, nonfinite_out, stream=None) -> None:
+    _check(_lib.zero_flatten_grads_sqnorm(_addr(segs_dev), n_segs, dtype, _addr(shard), shard_numel, _addr(ws),
+                                          ws_bytes, _addr(sqnorm_out), _addr(nonfinite_out), _stream(stream)))
+
+
+def zero_state_tiled_numel(n: int) -> int:
+    return int(_lib.zero_state_tiled_numel(n))
+
+
+def zero_adamw_step_tiled(grad, dtype: int, state, param, n: int, *, lr: float, beta1: float, beta2: float,
+                          eps: float, weight_decay: float, grad_scale: float, step: int, stream=None) -> None:
+    hp = zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, grad_scale, step)
+    _check(_lib.zero_adamw_step_tiled(_addr(grad), dtype, _addr(state), _addr(param), n, C.byref(hp),
+                                      _stream(stream)))
+
+
+def zero_state_tile(master, m, v, state, n: int, stream=None) -> None:
+    _check(_lib.zero_state_tile(_addr(master), _addr(m), _addr(v), _addr(state), n, _stream(stream)))
+
+
+def zero_state_untile(state, master, m, v, n: int, stream=None) -> None:
+    _check(_lib.zero_state_untile(_addr(state), _addr(master), _addr(m), _addr(v), n, _stream(stream)))

@@ -8,12 +8,13 @@ arithmetic of the method happens here; the decision is the library's
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 
 import torch
 
-from . import (ZERO_BF16, ZERO_FP16, zero_adamw_step, zero_flatten_grads, zero_flatten_plan,
-               zero_grad_sqnorm, zero_grad_sqnorm_workspace_bytes, zero_shard_layout, zero_step_decision)
+from . import (ZERO_BF16, ZERO_FP16, ZERO_STATE_TILE, zero_adamw_step, zero_adamw_step_tiled, zero_flatten_grads,
+               zero_flatten_grads_sqnorm, zero_flatten_plan, zero_grad_sqnorm, zero_grad_sqnorm_workspace_bytes,
+               zero_shard_layout, zero_state_tile, zero_state_tiled_numel, zero_state_untile, zero_step_decision)
 
 _TORCH16 = {ZERO_BF16: torch.bfloat16, ZERO_FP16: torch.float16}
 
@@ -38,18 +39,25 @@ class ScalerState:
 
 
 class RankShard:
-    """One simulated rank: the flat 16-bit grad shard, fp32 master/m/v, bf16 param and norm scratch."""
+    """One simulated rank: the flat 16-bit grad shard, the fp32 master/m/v state (three arrays, or one
+    tiled array when ``tiled``), the bf16 param shard and the norm scratch."""
 
-    def __init__(self, numels, world: int, rank: int, grad_dtype: int, device="cuda", sources=None):
+    def __init__(self, numels, world: int, rank: int, grad_dtype: int, device="cuda", sources=None,
+                 tiled: bool = False, fused: bool = False):
         self.layout, self.segments = zero_shard_layout(numels, world, rank)
         self.grad_dtype = grad_dtype
         self.device = torch.device(device)
+        self.tiled = tiled
+        self.fused = fused  # flatten and square-norm in one pass
         n = self.layout.shard_numel
         self.n = n
         self.grad = torch.empty(n, dtype=_TORCH16[grad_dtype], device=self.device)
-        self.master = torch.zeros(n, dtype=torch.float32, device=self.device)
-        self.m = torch.zeros(n, dtype=torch.float32, device=self.device)
-        self.v = torch.zeros(n, dtype=torch.float32, device=self.device)
+        if tiled:
+            self.state = torch.zeros(zero_state_tiled_numel(n), dtype=torch.float32, device=self.device)
+        else:
+            self.master = torch.zeros(n, dtype=torch.float32, device=self.device)
+            self.m = torch.zeros(n, dtype=torch.float32, device=self.device)
+            self.v = torch.zeros(n, dtype=torch.float32, device=self.device)
         self.param = torch.zeros(n, dtype=torch.bfloat16, device=self.device)
         self.ws_bytes = zero_grad_sqnorm_workspace_bytes(n)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
@@ -62,6 +70,40 @@ class RankShard:
         if sources is not None:
             self.set_sources(sources)
 
+    # -- state access (initialisation and checks) -------------------------------------------------
+
+    def load_master(self, master: torch.Tensor) -> None:
+        """Sets the fp32 master shard (device tensor of n floats); m and v start at zero."""
+        if self.tiled:
+            zeros = torch.zeros(self.n, dtype=torch.float32, device=self.device)
+            zero_state_tile(master, zeros, zeros, self.state, self.n)
+        else:
+            self.master.copy_(master)
+            self.m.zero_()
+            self.v.zero_()
+
+    def state_views(self, lo: int = 0, hi: int | None = None):
+        """(master, m, v) device tensors for shard elements [lo, hi).  With the tiled layout lo and hi must
+        be tile-aligned (hi may be n)."""
+        hi = self.n if hi is None else hi
+        if not self.tiled:
+            return self.master[lo:hi], self.m[lo:hi], self.v[lo:hi]
+        t = ZERO_STATE_TILE
+        assert lo % t == 0 and (hi % t == 0 or hi == self.n)
+        tiles = self.state.view(-1, 3, t)[lo // t: (hi + t - 1) // t]
+        cnt = hi - lo
+        return tuple(tiles[:, k, :].reshape(-1)[:cnt] for k in range(3))
+
+    def read_state(self):
+        """Whole (master, m, v) as separate device tensors (untiling when needed)."""
+        if not self.tiled:
+            return self.master, self.m, self.v
+        out = [torch.empty(self.n, dtype=torch.float32, device=self.device) for _ in range(3)]
+        zero_state_untile(self.state, *out, self.n)
+        return tuple(out)
+
+    # -- the step ------------------------------------------------------------------------------
+
     def set_sources(self, sources) -> None:
         """sources[t]: device tensor (or address) of tensor t's gradient; only tensors that land in the
         shard need one."""
@@ -73,11 +115,19 @@ class RankShard:
         self._sources = sources  # keep the tensors alive
 
     def flatten(self, stream=None) -> None:
-        zero_flatten_grads(self.seg_table, self.n_segs, self.grad_dtype, self.grad, self.n, stream)
+        if self.fused:
+            zero_flatten_grads_sqnorm(self.seg_table, self.n_segs, self.grad_dtype, self.grad, self.n, self.ws,
+                                      self.ws_bytes, self.sq_dev, self.flag_dev, stream)
+        else:
+            zero_flatten_grads(self.seg_table, self.n_segs, self.grad_dtype, self.grad, self.n, stream)
 
     def sqnorm(self, stream=None) -> None:
+        """Square-norm and non-finite flag of the shard as it stands (a separate pass)."""
         zero_grad_sqnorm(self.grad, self.grad_dtype, self.n, self.ws, self.ws_bytes, self.sq_dev, self.flag_dev,
                          stream)
+
+    def readback(self) -> None:
+        """Queue the 12-byte copy of the square-norm and flag to pinned host memory."""
         self.sq_host.copy_(self.sq_dev, non_blocking=True)
         self.flag_host.copy_(self.flag_dev, non_blocking=True)
 
@@ -86,9 +136,12 @@ class RankShard:
         return float(self.sq_host[0]), int(self.flag_host[0])
 
     def adamw(self, cfg: AdamWConfig, grad_scale: float, step: int, stream=None) -> None:
-        zero_adamw_step(self.grad, self.grad_dtype, self.master, self.m, self.v, self.param, self.n, lr=cfg.lr,
-                        beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, weight_decay=cfg.weight_decay,
-                        grad_scale=grad_scale, step=step, stream=stream)
+        kw = dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, weight_decay=cfg.weight_decay,
+                  grad_scale=grad_scale, step=step, stream=stream)
+        if self.tiled:
+            zero_adamw_step_tiled(self.grad, self.grad_dtype, self.state, self.param, self.n, **kw)
+        else:
+            zero_adamw_step(self.grad, self.grad_dtype, self.master, self.m, self.v, self.param, self.n, **kw)
 
 
 def rank_step(shards, cfg: AdamWConfig, scaler: ScalerState, flatten: bool = True, stream=None) -> dict:
@@ -96,7 +149,9 @@ def rank_step(shards, cfg: AdamWConfig, scaler: ScalerState, flatten: bool = Tru
     for sh in shards:
         if flatten:
             sh.flatten(stream)
-        sh.sqnorm(stream)
+        if not (flatten and sh.fused):
+            sh.sqnorm(stream)
+        sh.readback()
     (stream or torch.cuda.current_stream()).synchronize()
     sq, fl = zip(*(sh.norm_result() for sh in shards))
     dec = zero_step_decision(sq, fl, cfg.max_norm, scaler.scale, scaler.good_steps, scaler.growth_interval)

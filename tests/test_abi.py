@@ -145,3 +145,20 @@ def test_single_hip_runtime():
     synth._load()
     paths = Z.hip_runtimes_loaded()
     assert len(paths) == 1 and "torch" in paths[0], paths
+
+
+def test_tiled_numel_and_invalid_tiled_args():
+    assert Z.zero_state_tiled_numel(0) == 0
+    assert Z.zero_state_tiled_numel(1) == 3 * 1024
+    assert Z.zero_state_tiled_numel(1024) == 3 * 1024
+    assert Z.zero_state_tiled_numel(1025) == 6 * 1024
+    lib = Z.library()
+    hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 1)
+    assert lib.zero_adamw_step_tiled(16, 0, 24, 16, 8, hp, None) == Z.ZERO_ERR_INVALID  # state not 16-B aligned
+    assert lib.zero_adamw_step_tiled(16, 0, None, 16, 8, hp, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_adamw_step_tiled(17, 0, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_state_tile(None, 16, 16, 16, 5, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_state_untile(16, 16, 16, 16, -1, None) == Z.ZERO_ERR_INVALID
+    ws = Z.zero_grad_sqnorm_workspace_bytes(100)
+    assert lib.zero_flatten_grads_sqnorm(16, 1, 0, 16, 100, 256, ws - 1, 16, 16, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_flatten_grads_sqnorm(12, 1, 0, 16, 100, 256, ws, 16, 16, None) == Z.ZERO_ERR_INVALID

@@ -71,13 +71,27 @@ def _flatten_case(numels, world, src_offsets, dt, seed):
         s = lay.shard_numel
         table = Z.zero_flatten_plan(segs, srcs)
         tab = torch.frombuffer(bytearray(table or b"\0" * 32), dtype=torch.uint8).to(DEV)
+        ref = oracle.flatten(host, numels, world, rank)
+        rsq, rflag = oracle.sqnorm(ref, dt)
         for dst_off in (0, 3):
-            sbuf, shard = guarded(s, tdt, dst_off)
-            Z.zero_flatten_grads(tab, len(segs), dt, shard, s)
-            torch.cuda.synchronize()
-            ref = oracle.flatten(host, numels, world, rank)
-            assert_bits_equal(bits16(shard), ref, f"flatten rank {rank}/{world} dst_off {dst_off}")
-            check_guards(sbuf, dst_off, s, "flatten shard")
+            for fused in (False, True):
+                sbuf, shard = guarded(s, tdt, dst_off)
+                if fused:
+                    wsb = Z.zero_grad_sqnorm_workspace_bytes(s)
+                    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+                    out = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+                    flag = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+                    Z.zero_flatten_grads_sqnorm(tab, len(segs), dt, shard, s, ws, wsb, out, flag)
+                else:
+                    Z.zero_flatten_grads(tab, len(segs), dt, shard, s)
+                torch.cuda.synchronize()
+                what = f"flatten rank {rank}/{world} dst_off {dst_off} fused {fused}"
+                assert_bits_equal(bits16(shard), ref, what)
+                check_guards(sbuf, dst_off, s, "flatten shard")
+                if fused:
+                    assert int(flag.cpu()[0]) == rflag, what
+                    if not rflag:
+                        assert_norm_close(float(out.cpu()[0]), rsq, s, what)
     for buf, off, h in zip(keep, src_offsets, host):
         check_guards(buf, off, len(h), "flatten source")
 
@@ -92,6 +106,36 @@ def test_flatten_ragged_lists(dt):
 def test_flatten_many_blocks_and_padding():
     # > 1 workgroup per piece, shard not a multiple of 8, last rank mostly padding
     _flatten_case([200_003, 65_536 * 5 + 3, 17], 7, [0, 8, 1], 0, 4)
+
+
+def test_flatten_fused_norm_finite_values():
+    """Finite gradients (the random-bit cases above are mostly flagged), norm compared with the oracle."""
+    rng = np.random.default_rng(8)
+    numels = [70_001, 3, 65_536 * 2 + 1, 999]
+    host = [oracle.f32_to_bf16((rng.standard_normal(n) * 1e-3).astype(np.float32)) for n in numels]
+    srcs = [to_dev16(h, torch.bfloat16) for h in host]
+    for world in (1, 3):
+        for rank in range(world):
+            lay, segs = Z.zero_shard_layout(numels, world, rank)
+            s = lay.shard_numel
+            tab = torch.frombuffer(bytearray(Z.zero_flatten_plan(segs, [x.data_ptr() for x in srcs])),
+                                   dtype=torch.uint8).to(DEV)
+            shard = torch.empty(s, dtype=torch.bfloat16, device=DEV)
+            wsb = Z.zero_grad_sqnorm_workspace_bytes(s)
+            ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+            out = torch.zeros(1, dtype=torch.float64, device=DEV)
+            flag = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+            Z.zero_flatten_grads_sqnorm(tab, len(segs), 0, shard, s, ws, wsb, out, flag)
+            torch.cuda.synchronize()
+            ref = oracle.flatten(host, numels, world, rank)
+            assert_bits_equal(bits16(shard), ref, "fused flatten")
+            rsq, rflag = oracle.sqnorm(ref, 0)
+            assert int(flag.cpu()[0]) == rflag == 0
+            assert_norm_close(float(out.cpu()[0]), rsq, s, f"fused norm {world}/{rank}")
+            a = float(out.cpu()[0])
+            Z.zero_flatten_grads_sqnorm(tab, len(segs), 0, shard, s, ws, wsb, out, flag)
+            torch.cuda.synchronize()
+            assert float(out.cpu()[0]) == a  # deterministic
 
 
 def test_flatten_all_padding_ranks():
@@ -242,3 +286,93 @@ def test_adamw_zero_padding_stays_zero():
 
 def test_adamw_empty_is_noop():
     Z.zero_adamw_step(0, 0, 0, 0, 0, 0, 0, grad_scale=1.0, step=1, **HP_SETS[0])
+
+
+# ----------------------------------------------------------------------------- tiled state
+
+def _tiled_case(n, dt, gq_offset, hp, steps, seed):
+    rng = np.random.default_rng(seed)
+    tdt = torch.bfloat16 if dt == 0 else torch.float16
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    tn = Z.zero_state_tiled_numel(n)
+    sbuf, state = guarded(tn, torch.float32, 0)
+    state.zero_()
+    zeros = torch.zeros(n, device=DEV)
+    Z.zero_state_tile(torch.from_numpy(p0).to(DEV), zeros, zeros, state, n)
+    qbuf, q = guarded(n, torch.bfloat16, gq_offset)
+    gbuf, g = guarded(n, tdt, gq_offset)
+    rp, rm, rv = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+    rq = np.zeros(n, np.uint16)
+    for t in range(1, steps + 1):
+        if dt == 0:
+            gb = oracle.f32_to_bf16((rng.standard_normal(n) * 1e-3).astype(np.float32))
+        else:
+            gb = (rng.standard_normal(n) * 60.0).astype(np.float16).view(np.uint16)
+        g.copy_(to_dev16(gb, tdt))
+        Z.zero_adamw_step_tiled(g, dt, state, q, n, grad_scale=0.5, step=t, **hp)
+        oracle.adamw_step(gb, dt, rp, rm, rv, rq, grad_scale=0.5, step=t, **hp)
+        out = [torch.empty(n, device=DEV) for _ in range(3)]
+        Z.zero_state_untile(state, *out, n)
+        torch.cuda.synchronize()
+        what = f"tiled n={n} dt={dt} off={gq_offset} t={t}"
+        nd = assert_f32_close(out[0].cpu().numpy(), rp, what + " master")
+        nd += assert_f32_close(out[1].cpu().numpy(), rm, what + " m")
+        nd += assert_f32_close(out[2].cpu().numpy(), rv, what + " v")
+        nd += assert_bf16_within_ulp(bits16(q), rq, what + " param")
+        assert nd == 0, what
+    check_guards(sbuf, 0, tn, "tiled state")
+    check_guards(qbuf, gq_offset, n, "tiled param")
+    # padding floats of the last tile are never written
+    if n % 1024:
+        tail = state.view(-1, 3, 1024)[-1][:, n % 1024:]
+        assert (tail == 0).all()
+
+
+@pytest.mark.parametrize("n", [1, 5, 1023, 1024, 1025, 4096 * 3 + 7, 100_003])
+@pytest.mark.parametrize("dt", [0, 1])
+def test_adamw_tiled_sizes(n, dt):
+    _tiled_case(n, dt, 0, HP_SETS[0], 2, n + 7 * dt)
+
+
+@pytest.mark.parametrize("off", [1, 2, 4])
+def test_adamw_tiled_unaligned_grad_param(off):
+    _tiled_case(5 * 1024 + 3, 0, off, HP_SETS[1], 2, off)
+
+
+def test_tiled_matches_separate_arrays_bitwise():
+    n = 300_001
+    rng = np.random.default_rng(31)
+    p0 = torch.from_numpy((rng.standard_normal(n) * 0.02).astype(np.float32)).to(DEV)
+    state = torch.zeros(Z.zero_state_tiled_numel(n), device=DEV)
+    zeros = torch.zeros(n, device=DEV)
+    Z.zero_state_tile(p0, zeros, zeros, state, n)
+    p, m, v = p0.clone(), zeros.clone(), zeros.clone()
+    q1 = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    q2 = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    for t in (1, 2, 3):
+        g = to_dev16(oracle.f32_to_bf16((rng.standard_normal(n) * 1e-3).astype(np.float32)), torch.bfloat16)
+        Z.zero_adamw_step(g, 0, p, m, v, q1, n, grad_scale=0.9, step=t, **HP_SETS[1])
+        Z.zero_adamw_step_tiled(g, 0, state, q2, n, grad_scale=0.9, step=t, **HP_SETS[1])
+    out = [torch.empty(n, device=DEV) for _ in range(3)]
+    Z.zero_state_untile(state, *out, n)
+    torch.cuda.synchronize()
+    for a, b in zip(out, (p, m, v)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(q1.view(torch.int16), q2.view(torch.int16))
+
+
+def test_tile_untile_roundtrip():
+    for n in (1, 1000, 1024, 2049, 77_777):
+        src = [torch.randn(n, device=DEV) for _ in range(3)]
+        state = torch.full((Z.zero_state_tiled_numel(n),), 7.0, device=DEV)
+        Z.zero_state_tile(*src, state, n)
+        back = [torch.empty(n, device=DEV) for _ in range(3)]
+        Z.zero_state_untile(state, *back, n)
+        torch.cuda.synchronize()
+        for a, b in zip(src, back):
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+        tiles = state.view(-1, 3, 1024)
+        assert torch.equal(tiles[:, 0, :].reshape(-1)[:n], src[0])
+        assert torch.equal(tiles[:, 2, :].reshape(-1)[:n], src[2])
+        if n % 1024:
+            assert (tiles[-1][:, n % 1024:] == 7.0).all()

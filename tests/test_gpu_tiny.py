@@ -21,14 +21,17 @@ def bits16(t):
     return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("separate_buffers", [True, False])
-def test_tiny_all_ranks(separate_buffers):
+@pytest.mark.parametrize("mode", ["arrays", "slices", "tiled", "tiled-fused", "arrays-fused"])
+def test_tiny_all_ranks(mode):
+    """arrays: separate master/m/v per rank; slices: the ranks' shards as slices of one flat buffer per
+    array; tiled: tiled optimizer state; -fused: flatten and square-norm in one pass."""
     w = WORKLOADS["tiny"]
     dev = torch.device("cuda:0")
     src = torch.empty(w.psi, dtype=torch.bfloat16, device=dev)
-    shards = [RankShard(w.numels, w.world, r, Z.ZERO_BF16, dev, sources=[src]) for r in w.ranks]
+    shards = [RankShard(w.numels, w.world, r, Z.ZERO_BF16, dev, sources=[src], tiled=mode.startswith("tiled"),
+                        fused=mode.endswith("fused")) for r in w.ranks]
     s = shards[0].n
-    if not separate_buffers:
+    if mode == "slices":
         # The four shards as disjoint slices of one padded flat buffer per array (ranks 1..3 start at
         # odd multiples of 4 bytes, so they take the element path).
         flat = {k: torch.zeros(w.world * s, dtype=torch.float32, device=dev) for k in ("master", "m", "v")}
@@ -48,7 +51,7 @@ def test_tiny_all_ranks(separate_buffers):
         lay = sh.layout
         p = np.zeros(s, np.float32)
         p[:lay.shard_valid] = master_all[lay.shard_offset:lay.shard_offset + lay.shard_valid]
-        sh.master.copy_(torch.from_numpy(p))
+        sh.load_master(torch.from_numpy(p).to(dev))
         ref.append(dict(p=p.copy(), m=np.zeros(s, np.float32), v=np.zeros(s, np.float32), q=np.zeros(s, np.uint16)))
     oscale, ogood, ostep = 1.0, 0, 0
 
@@ -79,13 +82,14 @@ def test_tiny_all_ranks(separate_buffers):
                               beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, grad_scale=od["grad_scale"],
                               step=ostep)
             what = f"step {t} rank {r}"
-            nd = assert_f32_close(sh.master.cpu().numpy(), R["p"], what + " master")
-            nd += assert_f32_close(sh.m.cpu().numpy(), R["m"], what + " m")
-            nd += assert_f32_close(sh.v.cpu().numpy(), R["v"], what + " v")
+            gp, gm, gv = (x.cpu().numpy() for x in sh.read_state())
+            nd = assert_f32_close(gp, R["p"], what + " master")
+            nd += assert_f32_close(gm, R["m"], what + " m")
+            nd += assert_f32_close(gv, R["v"], what + " v")
             nd += assert_bf16_within_ulp(bits16(sh.param), R["q"], what + " param")
             assert nd == 0, f"{what}: {nd} elements differ in bits (within tolerance)"
     # the one padding element of rank 3 stays +0 everywhere
     last = shards[-1]
     assert last.layout.shard_valid == s - 1
-    for x in (last.master, last.m, last.v):
+    for x in last.read_state():
         assert int(x[-1:].view(torch.int32).cpu()[0]) == 0
