@@ -144,8 +144,9 @@ class RankShard:
             zero_adamw_step(self.grad, self.grad_dtype, self.master, self.m, self.v, self.param, self.n, **kw)
 
 
-def rank_step(shards, cfg: AdamWConfig, scaler: ScalerState, flatten: bool = True, stream=None) -> dict:
-    """One training step over the simulated ranks; returns the decision (grad_scale, skip, norm, ...)."""
+def rank_norms(shards, cfg: AdamWConfig, scaler: ScalerState, flatten: bool = True, stream=None) -> dict:
+    """First half of a step over the simulated ranks: flatten (and square-norm), the 12-byte readback, the
+    simulated all-reduce and the decision.  Updates the loss-scale state; returns the decision."""
     for sh in shards:
         if flatten:
             sh.flatten(stream)
@@ -156,10 +157,22 @@ def rank_step(shards, cfg: AdamWConfig, scaler: ScalerState, flatten: bool = Tru
     sq, fl = zip(*(sh.norm_result() for sh in shards))
     dec = zero_step_decision(sq, fl, cfg.max_norm, scaler.scale, scaler.good_steps, scaler.growth_interval)
     scaler.scale, scaler.good_steps = dec["loss_scale"], dec["good_steps"]
-    if not dec["skip"]:
-        scaler.adam_step += 1
-        for sh in shards:
-            sh.adamw(cfg, dec["grad_scale"], scaler.adam_step, stream)
     dec["rank_sqnorms"] = list(sq)
     dec["rank_flags"] = list(fl)
+    return dec
+
+
+def rank_update(shards, cfg: AdamWConfig, scaler: ScalerState, dec: dict, stream=None) -> None:
+    """Second half: the AdamW update of every simulated rank with the decision's factor (nothing on skip)."""
+    if dec["skip"]:
+        return
+    scaler.adam_step += 1
+    for sh in shards:
+        sh.adamw(cfg, dec["grad_scale"], scaler.adam_step, stream)
+
+
+def rank_step(shards, cfg: AdamWConfig, scaler: ScalerState, flatten: bool = True, stream=None) -> dict:
+    """One training step over the simulated ranks; returns the decision (grad_scale, skip, norm, ...)."""
+    dec = rank_norms(shards, cfg, scaler, flatten, stream)
+    rank_update(shards, cfg, scaler, dec, stream)
     return dec

@@ -76,8 +76,12 @@ class Workload:
     def psi(self) -> int:
         return int(sum(self.numels))
 
-    def grad_field(self, step: int) -> Field:
-        scale = self.loss_scale if self.grad_kind == FP16 else 1.0
+    def grad_field(self, step: int, loss_scale: float | None = None) -> Field:
+        """Gradients of `step`, stored multiplied by the loss scale in force (fp16 configurations)."""
+        if self.grad_kind == FP16:
+            scale = self.loss_scale if loss_scale is None else loss_scale
+        else:
+            scale = 1.0
         return make_field(self.seed, STREAM_GRAD, step, self.grad_sigma, self.grad_kind, scale,
                           self.outlier_per_million, self.outlier_sigma)
 

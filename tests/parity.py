@@ -65,3 +65,12 @@ def assert_norm_close(got: float, ref: float, n: int, what: str) -> None:
     # Any summation order of n non-negative fp64 terms stays within n·2^-53 of the exact sum, and so does
     # the sequential oracle: the two can differ by at most twice that.
     assert rel <= 2 * max(n, 1) * 2.0**-53, f"{what}: relative error {rel:.3e} beyond fp64 summation bound"
+
+
+def assert_grad_scale_close(got: float, ref: float, n: int, what: str) -> bool:
+    """The clip/unscale factor comes from each side's own fp64 square-norm; two summation orders of n terms
+    differ by at most 2·n·2^-53 relative, the square root halves that, the division adds rounding.
+    Returns True when both factors round to the same fp32 value (then the updates must agree bit for bit)."""
+    bound = max(1e-13, 2 * max(n, 1) * 2.0**-53)
+    assert abs(got - ref) <= bound * abs(ref), f"{what}: grad scale {got!r} vs {ref!r}"
+    return bool(np.float32(got) == np.float32(ref))
