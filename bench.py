@@ -19,6 +19,7 @@ write master/m/v 12 + param 2).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -62,6 +63,22 @@ def copy_calibration(nbytes: int, reps: int = 10) -> None:
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter record, or None when there is no record
+    for this kernel and workload or the kernel source has changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "mixed_precision_adam_amd", "csrc", "zero_shard.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec["bytes_per_launch"]
 
 
 def cpu_baseline(w, sample: int, steps: int) -> dict:
@@ -117,7 +134,7 @@ def main():
 
     import mixed_precision_adam_amd as Z
     import synth
-    from mixed_precision_adam_amd.driver import AdamWConfig, RankShard, ScalerState
+    from mixed_precision_adam_amd.driver import AdamWConfig, RankShard, ScalerState, wait_spin
     from synth.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
@@ -152,35 +169,44 @@ def main():
     torch.cuda.synchronize()
 
     ev = {k: [] for k in ("flatten", "sqnorm", "adamw")}
+    numels_c = (ctypes.c_int64 * len(w.numels))(*w.numels)
+    lay_out = Z.zero_layout()
+    nseg = ctypes.c_int32(0)
+    seg_buf = (Z.zero_segment * len(segs))()
+    lib = Z.library()
+    # events for the timed steps are created up front, outside the timed region
+    pool = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
 
-    def step(record: bool):
+    def step(e=None):
         # a1: layout (host) -- recomputed every step as part of the path
-        Z.zero_shard_layout(w.numels, w.world, rank)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if record else None
-        if record:
+        rc = lib.zero_shard_layout(ctypes.cast(numels_c, ctypes.c_void_p), len(w.numels), w.world, rank,
+                                   ctypes.byref(lay_out), ctypes.cast(seg_buf, ctypes.c_void_p), len(segs),
+                                   ctypes.byref(nseg))
+        assert rc == 0 and nseg.value == len(segs)
+        if e:
             e[0].record(stream)
-        sh.flatten()                                   # a2 (+ a3 when fused)
-        if record:
+        sh.flatten(stream)                             # a2 (+ a3 when fused)
+        if e:
             e[1].record(stream)
             e[2].record(stream)
         if not sh.fused:
-            sh.sqnorm()                                # a3
-        if record:
+            sh.sqnorm(stream)                          # a3
+        if e:
             e[3].record(stream)
-        sh.readback()                                  # 12 bytes to the host
-        stream.synchronize()
+        sh.readback()                                  # 16 bytes to the host
+        wait_spin(stream)
         sq, fl = sh.norm_result()                      # a4: host decision
         dec = Z.zero_step_decision([sq], [fl], cfg.max_norm, scaler.scale, scaler.good_steps,
                                    scaler.growth_interval)
         scaler.scale, scaler.good_steps = dec["loss_scale"], dec["good_steps"]
         if not dec["skip"]:
             scaler.adam_step += 1
-            if record:
+            if e:
                 e[4].record(stream)
-            sh.adamw(cfg, dec["grad_scale"], scaler.adam_step)   # a5
-            if record:
+            sh.adamw(cfg, dec["grad_scale"], scaler.adam_step, stream)   # a5
+            if e:
                 e[5].record(stream)
-        if record:
+        if e:
             ev["flatten"].append((e[0], e[1]))
             ev["sqnorm"].append((e[2], e[3]))
             if not dec["skip"]:
@@ -188,14 +214,14 @@ def main():
         return dec
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
 
     # timed region: K whole steps, synchronized on both sides (one process: no barrier needed)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        dec = step(True)
+    for k in range(args.steps):
+        dec = step(pool[k])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -233,7 +259,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": adam_gbs / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("adamw_tiled_kernel" if sh.tiled else "adamw_vec_kernel", w.name),
             "bytes_per_param": ADAM_BYTES_PER_PARAM,
         },
         "breakdown": {

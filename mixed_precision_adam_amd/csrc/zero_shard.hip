@@ -133,16 +133,41 @@ __device__ __forceinline__ u32x2 adam_unit4(u32x2 g, f32x4& p, f32x4& m, f32x4& 
   return out;
 }
 
+// The last, partial group of four elements (at most one per launch): element
+// by element, touching nothing at or past n.
+template <int DT>
+__device__ __forceinline__ void adam_partial4(const uint16_t* __restrict__ grad, float* __restrict__ p,
+                                              float* __restrict__ m, float* __restrict__ v,
+                                              uint16_t* __restrict__ param, int64_t e, int64_t n,
+                                              const AdamScalars& s) {
+  for (int64_t i = e; i < n; ++i) {
+    float pi = p[i - e], mi = m[i - e], vi = v[i - e];
+    adam_element(widen<DT>(grad[i]), pi, mi, vi, s);
+    p[i - e] = pi;
+    m[i - e] = mi;
+    v[i - e] = vi;
+    param[i] = static_cast<uint16_t>(bf16_rne(pi));
+  }
+}
+
 // Separate master / m / v arrays.  Unit u of workgroup b covers elements
 // 4·(b·U·256 + u·256 + t) .. +3 for thread t, so every load and store
 // instruction of a wavefront touches one contiguous span (1 KiB for the fp32
 // arrays, 512 B for grads and params).  All loads of the workgroup's U units
-// are issued before the arithmetic.
+// are issued before the arithmetic.  The thread whose group straddles n
+// finishes the ragged tail element by element.
 template <int DT, int U>
-__global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const u32x2* __restrict__ grad, f32x4* __restrict__ master,
-                                                           f32x4* __restrict__ mom, f32x4* __restrict__ var,
-                                                           u32x2* __restrict__ param, int64_t n4, AdamScalars s) {
+__global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const uint16_t* __restrict__ grad16,
+                                                           float* __restrict__ master, float* __restrict__ mom,
+                                                           float* __restrict__ var, uint16_t* __restrict__ param16,
+                                                           int64_t n, AdamScalars s) {
+  const int64_t n4 = n >> 2;
   const int64_t first = static_cast<int64_t>(blockIdx.x) * (kBlock * U) + threadIdx.x;
+  const u32x2* grad = reinterpret_cast<const u32x2*>(grad16);
+  f32x4* p4 = reinterpret_cast<f32x4*>(master);
+  f32x4* m4 = reinterpret_cast<f32x4*>(mom);
+  f32x4* v4 = reinterpret_cast<f32x4*>(var);
+  u32x2* param = reinterpret_cast<u32x2*>(param16);
   u32x2 g[U];
   f32x4 p[U], m[U], v[U];
 #pragma unroll
@@ -150,9 +175,9 @@ __global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const u32x2* __restri
     const int64_t i = first + static_cast<int64_t>(u) * kBlock;
     if (i < n4) {
       g[u] = ld_stream(grad + i);
-      p[u] = ld_stream(master + i);
-      m[u] = ld_stream(mom + i);
-      v[u] = ld_stream(var + i);
+      p[u] = ld_stream(p4 + i);
+      m[u] = ld_stream(m4 + i);
+      v[u] = ld_stream(v4 + i);
     }
   }
 #pragma unroll
@@ -160,10 +185,13 @@ __global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const u32x2* __restri
     const int64_t i = first + static_cast<int64_t>(u) * kBlock;
     if (i < n4) {
       const u32x2 q = adam_unit4<DT>(g[u], p[u], m[u], v[u], s);
-      st_stream(master + i, p[u]);
-      st_stream(mom + i, m[u]);
-      st_stream(var + i, v[u]);
+      st_stream(p4 + i, p[u]);
+      st_stream(m4 + i, m[u]);
+      st_stream(v4 + i, v[u]);
       st_stream(param + i, q);
+    } else if (i == n4 && 4 * n4 < n) {
+      const int64_t e = 4 * n4;
+      adam_partial4<DT>(grad16, master + e, mom + e, var + e, param16, e, n, s);
     }
   }
 }
@@ -173,26 +201,33 @@ constexpr int kAdamUnroll = 2;
 // Tiled optimizer state (ZERO_STATE_TILE = 1024 elements per tile): tile k
 // stores master, m and v of elements [1024k, 1024k+1024) back to back, so the
 // update streams three address ranges (grad, state, param) instead of five.
-// One workgroup per full tile; thread t owns elements 4t .. 4t+3 of it.
+// One workgroup per tile; thread t owns elements 4t .. 4t+3 of it.  In the
+// last tile, groups past n are skipped and the group straddling n is updated
+// element by element (the tile's padding floats keep their bits).
 constexpr int64_t kTile = ZERO_STATE_TILE;
 constexpr int64_t kTile4 = kTile / 4;  // 16-byte vectors per array per tile
 static_assert(kTile4 == kBlock, "one thread per 4 elements of a tile");
 
 template <int DT>
-__global__ __launch_bounds__(kBlock) void adamw_tiled_kernel(const u32x2* __restrict__ grad, f32x4* __restrict__ state,
-                                                             u32x2* __restrict__ param, int64_t full_tiles,
+__global__ __launch_bounds__(kBlock) void adamw_tiled_kernel(const uint16_t* __restrict__ grad16,
+                                                             f32x4* __restrict__ state,
+                                                             uint16_t* __restrict__ param16, int64_t n,
                                                              AdamScalars s) {
   const int64_t tile = blockIdx.x;
-  if (tile >= full_tiles) return;
-  const int64_t e4 = tile * kTile4 + threadIdx.x;
+  const int64_t e = tile * kTile + 4 * static_cast<int64_t>(threadIdx.x);
   f32x4* st = state + tile * (3 * kTile4) + threadIdx.x;
-  const u32x2 g = ld_stream(grad + e4);
-  f32x4 p = ld_stream(st), m = ld_stream(st + kTile4), v = ld_stream(st + 2 * kTile4);
-  const u32x2 q = adam_unit4<DT>(g, p, m, v, s);
-  st_stream(st, p);
-  st_stream(st + kTile4, m);
-  st_stream(st + 2 * kTile4, v);
-  st_stream(param + e4, q);
+  if (e + 4 <= n) {
+    const u32x2 g = ld_stream(reinterpret_cast<const u32x2*>(grad16 + e));
+    f32x4 p = ld_stream(st), m = ld_stream(st + kTile4), v = ld_stream(st + 2 * kTile4);
+    const u32x2 q = adam_unit4<DT>(g, p, m, v, s);
+    st_stream(st, p);
+    st_stream(st + kTile4, m);
+    st_stream(st + 2 * kTile4, v);
+    st_stream(reinterpret_cast<u32x2*>(param16 + e), q);
+  } else if (e < n) {
+    float* f = reinterpret_cast<float*>(st);
+    adam_partial4<DT>(grad16, f, f + kTile, f + 2 * kTile, param16, e, n, s);
+  }
 }
 
 // Element paths for ragged tails and unaligned buffers: the same update, one
@@ -754,27 +789,21 @@ int zero_adamw_step(const void* grad_dev, zero_dtype gdt, float* master_dev, flo
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool vec = aligned8(grad_dev) && aligned8(param_dev) && aligned16(master_dev) && aligned16(m_dev) &&
                    aligned16(v_dev);
-  const int64_t n4 = vec ? n / 4 : 0;
-  if (n4 > 0) {
-    constexpr int64_t per = kBlock * kAdamUnroll;
-    const int64_t blocks = (n4 + per - 1) / per;
-    auto* g = static_cast<const u32x2*>(grad_dev);
-    auto* p = reinterpret_cast<f32x4*>(master_dev);
-    auto* m = reinterpret_cast<f32x4*>(m_dev);
-    auto* v = reinterpret_cast<f32x4*>(v_dev);
-    auto* q = reinterpret_cast<u32x2*>(param_dev);
-    if (gdt == ZERO_BF16) {
-      hipLaunchKernelGGL((adamw_vec_kernel<ZERO_BF16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock),
-                         0, st, g, p, m, v, q, n4, s);
-    } else {
-      hipLaunchKernelGGL((adamw_vec_kernel<ZERO_FP16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock),
-                         0, st, g, p, m, v, q, n4, s);
-    }
-    rc = launch_status("zero_adamw_step (vector)");
-    if (rc != ZERO_OK) return rc;
+  if (!vec)
+    return launch_elements<false>(static_cast<const uint16_t*>(grad_dev), gdt, master_dev, m_dev, v_dev, param_dev,
+                                  0, n, s, st, "zero_adamw_step (elements)");
+  constexpr int64_t per = kBlock * kAdamUnroll;
+  const int64_t groups = (n + 3) / 4;  // the last one may be partial
+  const int64_t blocks = (groups + per - 1) / per;
+  const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
+  if (gdt == ZERO_BF16) {
+    hipLaunchKernelGGL((adamw_vec_kernel<ZERO_BF16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                       st, g, master_dev, m_dev, v_dev, param_dev, n, s);
+  } else {
+    hipLaunchKernelGGL((adamw_vec_kernel<ZERO_FP16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                       st, g, master_dev, m_dev, v_dev, param_dev, n, s);
   }
-  return launch_elements<false>(static_cast<const uint16_t*>(grad_dev), gdt, master_dev, m_dev, v_dev, param_dev,
-                                4 * n4, n, s, st, "zero_adamw_step (elements)");
+  return launch_status("zero_adamw_step");
 }
 
 int64_t zero_state_tiled_numel(int64_t n) {
@@ -791,23 +820,20 @@ int zero_adamw_step_tiled(const void* grad_dev, zero_dtype gdt, float* state_dev
   if (!aligned16(state_dev)) return fail(ZERO_ERR_INVALID, "zero_adamw_step_tiled: state must be 16-byte aligned");
   if (n == 0) return ZERO_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t full = (aligned8(grad_dev) && aligned8(param_dev)) ? n / kTile : 0;
-  if (full > 0) {
-    auto* g = static_cast<const u32x2*>(grad_dev);
-    auto* q = reinterpret_cast<u32x2*>(param_dev);
-    auto* state = reinterpret_cast<f32x4*>(state_dev);
-    if (gdt == ZERO_BF16) {
-      hipLaunchKernelGGL(adamw_tiled_kernel<ZERO_BF16>, dim3(static_cast<unsigned>(full)), dim3(kBlock), 0, st, g,
-                         state, q, full, s);
-    } else {
-      hipLaunchKernelGGL(adamw_tiled_kernel<ZERO_FP16>, dim3(static_cast<unsigned>(full)), dim3(kBlock), 0, st, g,
-                         state, q, full, s);
-    }
-    rc = launch_status("zero_adamw_step_tiled (tiles)");
-    if (rc != ZERO_OK) return rc;
+  const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
+  if (!aligned8(grad_dev) || !aligned8(param_dev))
+    return launch_elements<true>(g, gdt, state_dev, state_dev, state_dev, param_dev, 0, n, s, st,
+                                 "zero_adamw_step_tiled (elements)");
+  const int64_t tiles = (n + kTile - 1) / kTile;
+  auto* state = reinterpret_cast<f32x4*>(state_dev);
+  if (gdt == ZERO_BF16) {
+    hipLaunchKernelGGL(adamw_tiled_kernel<ZERO_BF16>, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, st, g,
+                       state, param_dev, n, s);
+  } else {
+    hipLaunchKernelGGL(adamw_tiled_kernel<ZERO_FP16>, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, st, g,
+                       state, param_dev, n, s);
   }
-  return launch_elements<true>(static_cast<const uint16_t*>(grad_dev), gdt, state_dev, state_dev, state_dev,
-                               param_dev, kTile * full, n, s, st, "zero_adamw_step_tiled (elements)");
+  return launch_status("zero_adamw_step_tiled");
 }
 
 int zero_state_tile(const float* master_dev, const float* m_dev, const float* v_dev, float* state_dev, int64_t n,

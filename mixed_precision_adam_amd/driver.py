@@ -10,6 +10,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 from . import (ZERO_BF16, ZERO_FP16, ZERO_STATE_TILE, zero_adamw_step, zero_adamw_step_tiled, zero_flatten_grads,
@@ -61,10 +62,12 @@ class RankShard:
         self.param = torch.zeros(n, dtype=torch.bfloat16, device=self.device)
         self.ws_bytes = zero_grad_sqnorm_workspace_bytes(n)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
-        self.sq_dev = torch.zeros(1, dtype=torch.float64, device=self.device)
-        self.flag_dev = torch.zeros(1, dtype=torch.int32, device=self.device)
-        self.sq_host = torch.zeros(1, dtype=torch.float64).pin_memory()
-        self.flag_host = torch.zeros(1, dtype=torch.int32).pin_memory()
+        # square-norm (double) and non-finite flag (int32) side by side: one 16-byte readback per step
+        self.norm_dev = torch.zeros(2, dtype=torch.float64, device=self.device)
+        self.sq_dev = self.norm_dev.data_ptr()
+        self.flag_dev = self.norm_dev.data_ptr() + 8
+        self.norm_host = torch.zeros(2, dtype=torch.float64).pin_memory()
+        self._norm_np = self.norm_host.numpy()
         self.seg_table = None
         self.n_segs = 0
         if sources is not None:
@@ -127,13 +130,12 @@ class RankShard:
                          stream)
 
     def readback(self) -> None:
-        """Queue the 12-byte copy of the square-norm and flag to pinned host memory."""
-        self.sq_host.copy_(self.sq_dev, non_blocking=True)
-        self.flag_host.copy_(self.flag_dev, non_blocking=True)
+        """Queue the 16-byte copy of the square-norm and flag to pinned host memory."""
+        self.norm_host.copy_(self.norm_dev, non_blocking=True)
 
     def norm_result(self):
         """Host copies of the last sqnorm; call after the stream has been synchronized."""
-        return float(self.sq_host[0]), int(self.flag_host[0])
+        return float(self._norm_np[0]), int(self._norm_np[1:2].view(np.int32)[0])
 
     def adamw(self, cfg: AdamWConfig, grad_scale: float, step: int, stream=None) -> None:
         kw = dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, weight_decay=cfg.weight_decay,
@@ -144,16 +146,26 @@ class RankShard:
             zero_adamw_step(self.grad, self.grad_dtype, self.master, self.m, self.v, self.param, self.n, **kw)
 
 
+def wait_spin(stream) -> None:
+    """Waits for the work queued on `stream` by polling an event: the decision that follows sits on the
+    critical path between the norm and the update, and polling wakes within microseconds of completion."""
+    done = torch.cuda.Event()
+    done.record(stream)
+    while not done.query():
+        pass
+
+
 def rank_norms(shards, cfg: AdamWConfig, scaler: ScalerState, flatten: bool = True, stream=None) -> dict:
-    """First half of a step over the simulated ranks: flatten (and square-norm), the 12-byte readback, the
+    """First half of a step over the simulated ranks: flatten (and square-norm), the 16-byte readback, the
     simulated all-reduce and the decision.  Updates the loss-scale state; returns the decision."""
+    stream = stream or torch.cuda.current_stream()
     for sh in shards:
         if flatten:
             sh.flatten(stream)
         if not (flatten and sh.fused):
             sh.sqnorm(stream)
         sh.readback()
-    (stream or torch.cuda.current_stream()).synchronize()
+    wait_spin(stream)
     sq, fl = zip(*(sh.norm_result() for sh in shards))
     dec = zero_step_decision(sq, fl, cfg.max_norm, scaler.scale, scaler.good_steps, scaler.growth_interval)
     scaler.scale, scaler.good_steps = dec["loss_scale"], dec["good_steps"]
@@ -166,6 +178,7 @@ def rank_update(shards, cfg: AdamWConfig, scaler: ScalerState, dec: dict, stream
     """Second half: the AdamW update of every simulated rank with the decision's factor (nothing on skip)."""
     if dec["skip"]:
         return
+    stream = stream or torch.cuda.current_stream()
     scaler.adam_step += 1
     for sh in shards:
         sh.adamw(cfg, dec["grad_scale"], scaler.adam_step, stream)
