@@ -44,6 +44,10 @@ def parse():
     ap.add_argument("--state", choices=("tiled", "arrays"), default="tiled",
                     help="optimizer-state layout: tiled master/m/v (default) or three separate arrays")
     ap.add_argument("--unfused", action="store_true", help="flatten and square-norm as two passes")
+    ap.add_argument("--decision", choices=("device", "host"), default="device",
+                    help="decision on the GPU (no host round trip, default) or on the host after a 16-byte readback")
+    ap.add_argument("--event-every", type=int, default=4,
+                    help="bracket the kernels of every k-th timed step with HIP events (each record costs ~3 us)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-sample", type=int, default=0, help="elements of the shard the oracle times (0: all)")
     ap.add_argument("--cpu-steps", type=int, default=3, help="steps the oracle times")
@@ -134,7 +138,7 @@ def main():
 
     import mixed_precision_adam_amd as Z
     import synth
-    from mixed_precision_adam_amd.driver import AdamWConfig, RankShard, ScalerState, wait_spin
+    from mixed_precision_adam_amd.driver import AdamWConfig, DeviceDecision, RankShard, ScalerState, wait_spin
     from synth.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
@@ -164,7 +168,10 @@ def main():
     del master0
     cfg = AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
                       max_norm=w.clip)
-    scaler = ScalerState(scale=w.loss_scale, growth_interval=2**31 - 1 if w.grad_kind == synth.BF16 else 1000)
+    growth = 2**31 - 1 if w.grad_kind == synth.BF16 else 1000
+    scaler = ScalerState(scale=w.loss_scale, growth_interval=growth)
+    ddec = DeviceDecision([sh], cfg, loss_scale=w.loss_scale, growth_interval=growth) if args.decision == "device" \
+        else None
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
@@ -174,7 +181,8 @@ def main():
     nseg = ctypes.c_int32(0)
     seg_buf = (Z.zero_segment * len(segs))()
     lib = Z.library()
-    # events for the timed steps are created up front, outside the timed region
+    # events for the timed steps are created up front, outside the timed region; they bracket the flatten
+    # and the update of every k-th step (a record costs a few microseconds of GPU time)
     pool = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
 
     def step(e=None):
@@ -183,6 +191,25 @@ def main():
                                    ctypes.byref(lay_out), ctypes.cast(seg_buf, ctypes.c_void_p), len(segs),
                                    ctypes.byref(nseg))
         assert rc == 0 and nseg.value == len(segs)
+        if ddec is not None:                           # everything on the GPU, nothing waits on the host
+            if e:
+                e[0].record(stream)
+            sh.flatten(stream)                         # a2 + a3 (fused)
+            if not sh.fused:
+                sh.sqnorm(stream)                      # a3
+            if e:
+                e[1].record(stream)
+            Z.zero_step_decision_dev(ddec.sq_base, ddec.flag_base, 1, cfg.max_norm, ddec.state, lr=cfg.lr,
+                                     beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps,
+                                     weight_decay=cfg.weight_decay, stream=stream)   # a4
+            if e:
+                e[4].record(stream)
+            sh.adamw_dev(ddec.state, stream)           # a5
+            if e:
+                e[5].record(stream)
+                ev["flatten"].append((e[0], e[1]))
+                ev["adamw"].append((e[4], e[5]))
+            return None
         if e:
             e[0].record(stream)
         sh.flatten(stream)                             # a2 (+ a3 when fused)
@@ -221,9 +248,13 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        dec = step(pool[k])
+        dec = step(pool[k] if k % args.event_every == args.event_every - 1 or args.steps < args.event_every else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+
+    if ddec is not None:
+        st = ddec.read()
+        dec = {"global_norm": st["global_norm"], "grad_scale": st["grad_scale"], "skip": st["skip"]}
 
     def avg_ms(pairs):
         return sum(a.elapsed_time(b) for a, b in pairs) / max(len(pairs), 1)
@@ -266,11 +297,13 @@ def main():
             "adamw_ms": ms["adamw"],
             "adamw_params_per_s": S / (ms["adamw"] * 1e-3),
             "state_layout": args.state,
+            "decision": args.decision,
             "flatten_norm_fused": sh.fused,
             "flatten_ms": ms["flatten"],
             "flatten_gbs": FLATTEN_BYTES_PER_PARAM * S / (ms["flatten"] * 1e-3) / 1e9,
-            "sqnorm_ms": ms["sqnorm"],
-            "sqnorm_gbs": (NORM_BYTES_PER_PARAM * S / (ms["sqnorm"] * 1e-3) / 1e9) if not sh.fused else None,
+            "sqnorm_ms": ms["sqnorm"] if ev["sqnorm"] else None,
+            "sqnorm_gbs": (NORM_BYTES_PER_PARAM * S / (ms["sqnorm"] * 1e-3) / 1e9) if ev["sqnorm"] and not sh.fused
+            else None,
             "step_bytes_per_param": step_bpp,
             "step_gbs_algorithmic": step_bpp * params_per_s / 1e9,
             "last_global_norm": dec["global_norm"],

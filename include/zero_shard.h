@@ -219,9 +219,9 @@ int zero_adamw_step(const void* grad_dev, zero_dtype gdt, float* master_dev, flo
 
 /* Tiled optimizer state: the same fp32 master / m / v, interleaved in tiles of
  * ZERO_STATE_TILE elements.  Tile k holds master[T·k .. T·k+T), then m[...],
- * then v[...] (T = ZERO_STATE_TILE, 12·T bytes per tile), so the update
+ * then v[...] (T = ZERO_STATE_TILE, 12·T = 12 KiB per tile), so the update
  * streams three address ranges (grad, state, param) instead of five; on
- * MI355X that is worth about 7% of achieved bandwidth.  A shard of n
+ * MI355X that is worth 7-20% of achieved bandwidth.  A shard of n
  * elements needs zero_state_tiled_numel(n) floats (the last tile is padded).
  * zero_adamw_step_tiled computes exactly what zero_adamw_step computes (same
  * per-element operations, same bits); state_dev must be 16-byte aligned. */
@@ -234,6 +234,51 @@ int zero_adamw_step_tiled(const void* grad_dev, zero_dtype gdt, float* state_dev
 int zero_state_tile(const float* master_dev, const float* m_dev, const float* v_dev, float* state_dev, int64_t n,
                     void* stream);
 int zero_state_untile(const float* state_dev, float* master_dev, float* m_dev, float* v_dev, int64_t n, void* stream);
+
+/* ------------------------------------------------------------------ device-resident decision
+ *
+ * The same decision (zero_step_decision) and scalar derivation (zero_adamw_step)
+ * evaluated by one GPU thread, so a step needs no host round trip between the
+ * norm and the update: flatten+norm -> zero_step_decision_dev ->
+ * zero_adamw_step_[tiled_]dev, all enqueued back to back on one stream (and
+ * capturable in a HIP graph: no memset, copy or host callback is involved).
+ * The state lives in caller-allocated device memory; read it back at will.
+ * The fp64 host arithmetic of the decision is repeated on the device with the
+ * same IEEE operations (correctly rounded +, -, *, /, sqrt); beta^t uses the
+ * device pow, which can differ from the host's in the last fp64 bit (then an
+ * fp32 scalar may differ by one ulp, in about 1 of 10^9 steps). */
+typedef struct zero_step_state {
+  double loss_scale;      /* current dynamic loss scale */
+  double global_norm;     /* unscaled global norm of the last decided step (NaN if skipped) */
+  double grad_scale;      /* factor of the last decided step: coef / loss scale (0 if skipped) */
+  int64_t adam_step;      /* Adam t of the last applied update */
+  int64_t iteration;      /* steps decided so far, skipped or not */
+  int32_t good_steps;     /* consecutive good steps since the last scale change */
+  int32_t growth_interval;
+  int32_t skip;           /* 1: the last decided step is skipped (the update kernels do nothing) */
+  int32_t reserved;
+  float scalars[12];      /* fp32 b1, 1-b1, b2, 1-b2, eps, 1-lr*wd, lr/(1-b1^t), sqrt(1-b2^t), gscale, 0, 0, 0 */
+} zero_step_state;
+
+/* Device.  Writes the initial state (loss scale, growth interval >= 1, t = 0)
+ * with a one-thread kernel.  state_dev: 16-byte aligned. */
+int zero_step_state_init(zero_step_state* state_dev, double loss_scale, int32_t growth_interval, void* stream);
+
+/* Device.  rank_sqnorms_dev[n_ranks] (double) and rank_flags_dev[n_ranks]
+ * (int32) as written by zero_grad_sqnorm / zero_flatten_grads_sqnorm; hp
+ * supplies lr, beta1, beta2, eps and weight_decay (hp->step and
+ * hp->grad_scale are ignored: t and the factor come from the state and the
+ * decision).  Updates *state_dev as described above. */
+int zero_step_decision_dev(const double* rank_sqnorms_dev, const int32_t* rank_flags_dev, int32_t n_ranks,
+                           double max_norm, const zero_adamw_hparams* hp, zero_step_state* state_dev, void* stream);
+
+/* Device.  zero_adamw_step / zero_adamw_step_tiled with the scalars taken
+ * from the device state; when state_dev->skip is set the kernels return
+ * without touching memory. */
+int zero_adamw_step_dev(const void* grad_dev, zero_dtype gdt, float* master_dev, float* m_dev, float* v_dev,
+                        uint16_t* param_dev, int64_t n, const zero_step_state* state_dev, void* stream);
+int zero_adamw_step_tiled_dev(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev, int64_t n,
+                              const zero_step_state* step_state_dev, void* stream);
 
 #ifdef __cplusplus
 }

@@ -92,13 +92,26 @@ _lib.zero_adamw_step_tiled.argtypes = [_P, C.c_int, _P, _P, C.c_int64, C.POINTER
 _lib.zero_state_tile.argtypes = [_P, _P, _P, _P, C.c_int64, _P]
 _lib.zero_state_untile.argtypes = [_P, _P, _P, _P, C.c_int64, _P]
 
-ZERO_STATE_TILE = 1024
+_lib.zero_step_state_init.argtypes = [_P, C.c_double, C.c_int32, _P]
+_lib.zero_step_decision_dev.argtypes = [_P, _P, C.c_int32, C.c_double, C.POINTER(zero_adamw_hparams), _P, _P]
+_lib.zero_adamw_step_dev.argtypes = [_P, C.c_int, _P, _P, _P, _P, C.c_int64, _P, _P]
+_lib.zero_adamw_step_tiled_dev.argtypes = [_P, C.c_int, _P, _P, C.c_int64, _P, _P]
+
+ZERO_STATE_TILE = 1024  # include/zero_shard.h
+
+
+class zero_step_state(C.Structure):
+    _fields_ = [("loss_scale", C.c_double), ("global_norm", C.c_double), ("grad_scale", C.c_double),
+                ("adam_step", C.c_int64), ("iteration", C.c_int64), ("good_steps", C.c_int32),
+                ("growth_interval", C.c_int32), ("skip", C.c_int32), ("reserved", C.c_int32),
+                ("scalars", C.c_float * 12)]
 
 # Every symbol include/zero_shard.h declares.
 EXPORTS = ("zero_last_error", "zero_shard_layout", "zero_flatten_plan", "zero_flatten_grads",
            "zero_flatten_grads_sqnorm", "zero_grad_sqnorm_workspace_bytes", "zero_grad_sqnorm", "zero_step_decision",
            "zero_clip_coef", "zero_loss_scale_update", "zero_cosine_lr", "zero_adamw_step", "zero_state_tiled_numel",
-           "zero_adamw_step_tiled", "zero_state_tile", "zero_state_untile")
+           "zero_adamw_step_tiled", "zero_state_tile", "zero_state_untile", "zero_step_state_init",
+           "zero_step_decision_dev", "zero_adamw_step_dev", "zero_adamw_step_tiled_dev")
 
 
 def library() -> C.CDLL:
@@ -241,3 +254,33 @@ def zero_state_tile(master, m, v, state, n: int, stream=None) -> None:
 
 def zero_state_untile(state, master, m, v, n: int, stream=None) -> None:
     _check(_lib.zero_state_untile(_addr(state), _addr(master), _addr(m), _addr(v), n, _stream(stream)))
+
+
+def zero_step_state_init(state, loss_scale: float, growth_interval: int, stream=None) -> None:
+    _check(_lib.zero_step_state_init(_addr(state), loss_scale, growth_interval, _stream(stream)))
+
+
+def zero_step_decision_dev(rank_sqnorms, rank_flags, n_ranks: int, max_norm: float, state, *, lr: float,
+                           beta1: float, beta2: float, eps: float, weight_decay: float, stream=None) -> None:
+    hp = zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, 1.0, 1)
+    _check(_lib.zero_step_decision_dev(_addr(rank_sqnorms), _addr(rank_flags), n_ranks, max_norm, C.byref(hp),
+                                       _addr(state), _stream(stream)))
+
+
+def zero_adamw_step_dev(grad, dtype: int, master, m, v, param, n: int, step_state, stream=None) -> None:
+    _check(_lib.zero_adamw_step_dev(_addr(grad), dtype, _addr(master), _addr(m), _addr(v), _addr(param), n,
+                                    _addr(step_state), _stream(stream)))
+
+
+def zero_adamw_step_tiled_dev(grad, dtype: int, state, param, n: int, step_state, stream=None) -> None:
+    _check(_lib.zero_adamw_step_tiled_dev(_addr(grad), dtype, _addr(state), _addr(param), n, _addr(step_state),
+                                          _stream(stream)))
+
+
+def read_step_state(state_tensor) -> dict:
+    """Copies a device zero_step_state (held in a torch tensor) to the host (synchronizes) and decodes it."""
+    raw = bytes(state_tensor.detach().cpu().view(-1).view(__import__("torch").uint8).numpy().tobytes())
+    st = zero_step_state.from_buffer_copy(raw[:C.sizeof(zero_step_state)])
+    out = {f: getattr(st, f) for f, _ in zero_step_state._fields_ if f != "scalars"}
+    out["scalars"] = list(st.scalars)[:9]
+    return out

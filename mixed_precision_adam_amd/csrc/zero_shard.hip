@@ -99,6 +99,24 @@ __device__ __forceinline__ void adam_element(float g, float& p, float& m, float&
   p = p_dec - u;
 }
 
+// Scalars of the update: by value from the host, or from the device-resident
+// step state when `dev` is given (then a skipped step leaves everything as is).
+// Every lane reads the same few bytes, so they come through the scalar cache.
+__device__ __forceinline__ bool take_scalars(const zero_step_state* dev, AdamScalars& s) {
+  if (dev == nullptr) return true;
+  if (dev->skip) return false;
+  s.b1 = dev->scalars[0];
+  s.omb1 = dev->scalars[1];
+  s.b2 = dev->scalars[2];
+  s.omb2 = dev->scalars[3];
+  s.eps = dev->scalars[4];
+  s.decay = dev->scalars[5];
+  s.step_size = dev->scalars[6];
+  s.bc2_sqrt = dev->scalars[7];
+  s.gscale = dev->scalars[8];
+  return true;
+}
+
 // Streaming accesses: every byte the update touches is used exactly once, so
 // loads and stores carry the non-temporal hint (measured on MI355X: +7% over
 // default caching for this kernel).
@@ -160,7 +178,7 @@ template <int DT, int U>
 __global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const uint16_t* __restrict__ grad16,
                                                            float* __restrict__ master, float* __restrict__ mom,
                                                            float* __restrict__ var, uint16_t* __restrict__ param16,
-                                                           int64_t n, AdamScalars s) {
+                                                           int64_t n, AdamScalars s, const zero_step_state* dev) {
   const int64_t n4 = n >> 2;
   const int64_t first = static_cast<int64_t>(blockIdx.x) * (kBlock * U) + threadIdx.x;
   const u32x2* grad = reinterpret_cast<const u32x2*>(grad16);
@@ -180,6 +198,7 @@ __global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const uint16_t* __res
       v[u] = ld_stream(v4 + i);
     }
   }
+  if (!take_scalars(dev, s)) return;  // after the data loads: they overlap with the scalar fetch
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t i = first + static_cast<int64_t>(u) * kBlock;
@@ -201,32 +220,55 @@ constexpr int kAdamUnroll = 2;
 // Tiled optimizer state (ZERO_STATE_TILE = 1024 elements per tile): tile k
 // stores master, m and v of elements [1024k, 1024k+1024) back to back, so the
 // update streams three address ranges (grad, state, param) instead of five.
-// One workgroup per tile; thread t owns elements 4t .. 4t+3 of it.  In the
-// last tile, groups past n are skipped and the group straddling n is updated
-// element by element (the tile's padding floats keep their bits).
+// One 256-thread workgroup per tile; thread t owns the group of four elements
+// 4t .. 4t+3 (kTileUnits groups in general, issuing every load before any
+// arithmetic).  Measured on MI355X, one group per thread and 12 KiB of state
+// per workgroup beats two groups / 24 KiB by 4%, provided every store carries
+// the non-temporal hint (without it the update loses 13%).  In the last tile,
+// groups past n are skipped and the group straddling n is updated element by
+// element (the tile's padding floats keep their bits).
 constexpr int64_t kTile = ZERO_STATE_TILE;
+constexpr int kTileUnits = 1;
 constexpr int64_t kTile4 = kTile / 4;  // 16-byte vectors per array per tile
-static_assert(kTile4 == kBlock, "one thread per 4 elements of a tile");
+static_assert(kTile4 == kBlock * kTileUnits, "each thread owns kTileUnits groups of 4 elements of a tile");
 
 template <int DT>
 __global__ __launch_bounds__(kBlock) void adamw_tiled_kernel(const uint16_t* __restrict__ grad16,
                                                              f32x4* __restrict__ state,
                                                              uint16_t* __restrict__ param16, int64_t n,
-                                                             AdamScalars s) {
+                                                             AdamScalars s, const zero_step_state* dev) {
   const int64_t tile = blockIdx.x;
-  const int64_t e = tile * kTile + 4 * static_cast<int64_t>(threadIdx.x);
-  f32x4* st = state + tile * (3 * kTile4) + threadIdx.x;
-  if (e + 4 <= n) {
-    const u32x2 g = ld_stream(reinterpret_cast<const u32x2*>(grad16 + e));
-    f32x4 p = ld_stream(st), m = ld_stream(st + kTile4), v = ld_stream(st + 2 * kTile4);
-    const u32x2 q = adam_unit4<DT>(g, p, m, v, s);
-    st_stream(st, p);
-    st_stream(st + kTile4, m);
-    st_stream(st + 2 * kTile4, v);
-    st_stream(reinterpret_cast<u32x2*>(param16 + e), q);
-  } else if (e < n) {
-    float* f = reinterpret_cast<float*>(st);
-    adam_partial4<DT>(grad16, f, f + kTile, f + 2 * kTile, param16, e, n, s);
+  f32x4* base = state + tile * (3 * kTile4);
+  u32x2 g[kTileUnits];
+  f32x4 p[kTileUnits], m[kTileUnits], v[kTileUnits];
+#pragma unroll
+  for (int u = 0; u < kTileUnits; ++u) {
+    const int j = threadIdx.x + u * kBlock;
+    const int64_t e = tile * kTile + 4 * static_cast<int64_t>(j);
+    if (e + 4 <= n) {
+      g[u] = ld_stream(reinterpret_cast<const u32x2*>(grad16 + e));
+      p[u] = ld_stream(base + j);
+      m[u] = ld_stream(base + kTile4 + j);
+      v[u] = ld_stream(base + 2 * kTile4 + j);
+    }
+  }
+  // The data loads above do not depend on the scalars, so they are in flight
+  // while the (device-resident) scalars arrive.
+  if (!take_scalars(dev, s)) return;
+#pragma unroll
+  for (int u = 0; u < kTileUnits; ++u) {
+    const int j = threadIdx.x + u * kBlock;
+    const int64_t e = tile * kTile + 4 * static_cast<int64_t>(j);
+    if (e + 4 <= n) {
+      const u32x2 q = adam_unit4<DT>(g[u], p[u], m[u], v[u], s);
+      st_stream(base + j, p[u]);
+      st_stream(base + kTile4 + j, m[u]);
+      st_stream(base + 2 * kTile4 + j, v[u]);
+      st_stream(reinterpret_cast<u32x2*>(param16 + e), q);
+    } else if (e < n) {
+      float* f = reinterpret_cast<float*>(base + j);
+      adam_partial4<DT>(grad16, f, f + kTile, f + 2 * kTile, param16, e, n, s);
+    }
   }
 }
 
@@ -236,7 +278,9 @@ template <int DT, bool TILED>
 __global__ __launch_bounds__(kBlock) void adamw_element_kernel(const uint16_t* __restrict__ grad,
                                                                float* __restrict__ master, float* __restrict__ mom,
                                                                float* __restrict__ var, uint16_t* __restrict__ param,
-                                                               int64_t begin, int64_t n, AdamScalars s) {
+                                                               int64_t begin, int64_t n, AdamScalars s,
+                                                               const zero_step_state* dev) {
+  if (!take_scalars(dev, s)) return;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock;
   for (int64_t i = begin + static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
     int64_t ip = i, im = i, iv = i;
@@ -387,10 +431,16 @@ __global__ __launch_bounds__(kBlock) void sqnorm_final_kernel(const double* __re
 // share their position inside a 16-byte line, a scalar head brings d to a
 // 16-byte boundary and the body moves 16-byte vectors.  With ACC the copied
 // values are also squared into acc (fp64) and checked for inf/NaN.
+// Source tensors are plain device allocations (global memory); saying so lets
+// the compiler use global rather than flat loads for them.
+typedef const u32x4 __attribute__((address_space(1)))* global_u32x4_ptr;
+typedef const uint16_t __attribute__((address_space(1)))* global_u16_ptr;
+
 template <int DT, bool ACC>
-__device__ void copy_piece(const uint16_t* __restrict__ s, uint16_t* __restrict__ d, int64_t len, double& acc,
+__device__ void copy_piece(const uint16_t* __restrict__ s_generic, uint16_t* __restrict__ d, int64_t len, double& acc,
                            uint32_t& bad) {
-  const uintptr_t ds = reinterpret_cast<uintptr_t>(d), ss = reinterpret_cast<uintptr_t>(s);
+  const global_u16_ptr s = (global_u16_ptr)s_generic;
+  const uintptr_t ds = reinterpret_cast<uintptr_t>(d), ss = reinterpret_cast<uintptr_t>(s_generic);
   int64_t head = len, nv = 0;
   if (((ds ^ ss) & 15u) == 0) {
     head = static_cast<int64_t>(((16u - (ds & 15u)) & 15u) >> 1);
@@ -402,14 +452,14 @@ __device__ void copy_piece(const uint16_t* __restrict__ s, uint16_t* __restrict_
     d[j] = x;
     if (ACC) accumulate<DT>(x, acc, bad);
   }
-  const u32x4* sv = reinterpret_cast<const u32x4*>(s + head);
+  const global_u32x4_ptr sv = (global_u32x4_ptr)(s + head);
   u32x4* dv = reinterpret_cast<u32x4*>(d + head);
-  constexpr int kU = 4;
+  constexpr int kU = 4;  // vectors in flight per thread (more than occupancy is worth here)
   int64_t j = threadIdx.x;
   for (; j + (kU - 1) * kBlock < nv; j += kU * kBlock) {
     u32x4 w[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) w[u] = ld_stream(sv + j + u * kBlock);
+    for (int u = 0; u < kU; ++u) w[u] = __builtin_nontemporal_load(sv + j + u * kBlock);
 #pragma unroll
     for (int u = 0; u < kU; ++u) st_stream(dv + j + u * kBlock, w[u]);
     if (ACC) {
@@ -418,7 +468,7 @@ __device__ void copy_piece(const uint16_t* __restrict__ s, uint16_t* __restrict_
     }
   }
   for (; j < nv; j += kBlock) {
-    const u32x4 w = ld_stream(sv + j);
+    const u32x4 w = __builtin_nontemporal_load(sv + j);
     st_stream(dv + j, w);
     if (ACC) accumulate8<DT>(w, acc, bad);
   }
@@ -533,17 +583,142 @@ int adam_args_ok(const char* fn, const void* grad_dev, int gdt, const void* para
 
 template <bool TILED>
 int launch_elements(const uint16_t* grad, int gdt, float* master, float* m, float* v, uint16_t* param, int64_t begin,
-                    int64_t n, const AdamScalars& s, hipStream_t st, const char* what) {
+                    int64_t n, const AdamScalars& s, const zero_step_state* dev, hipStream_t st, const char* what) {
   if (begin >= n) return ZERO_OK;
   const int64_t blocks = std::min<int64_t>((n - begin + kBlock - 1) / kBlock, 65536);
   if (gdt == ZERO_BF16) {
     hipLaunchKernelGGL((adamw_element_kernel<ZERO_BF16, TILED>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                       st, grad, master, m, v, param, begin, n, s);
+                       st, grad, master, m, v, param, begin, n, s, dev);
   } else {
     hipLaunchKernelGGL((adamw_element_kernel<ZERO_FP16, TILED>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                       st, grad, master, m, v, param, begin, n, s);
+                       st, grad, master, m, v, param, begin, n, s, dev);
   }
   return launch_status(what);
+}
+
+int launch_adamw_arrays(const char* fn, const void* grad_dev, int gdt, float* master_dev, float* m_dev, float* v_dev,
+                        uint16_t* param_dev, int64_t n, const AdamScalars& s, const zero_step_state* dev,
+                        hipStream_t st) {
+  if (n > 0 && (!master_dev || !m_dev || !v_dev)) return fail(ZERO_ERR_INVALID, "%s: NULL state", fn);
+  if (((reinterpret_cast<uintptr_t>(master_dev) | reinterpret_cast<uintptr_t>(m_dev) |
+        reinterpret_cast<uintptr_t>(v_dev)) & 3u) != 0)
+    return fail(ZERO_ERR_INVALID, "%s: fp32 buffers not 4-byte aligned", fn);
+  if (n == 0) return ZERO_OK;
+  const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
+  const bool vec = aligned8(grad_dev) && aligned8(param_dev) && aligned16(master_dev) && aligned16(m_dev) &&
+                   aligned16(v_dev);
+  if (!vec) return launch_elements<false>(g, gdt, master_dev, m_dev, v_dev, param_dev, 0, n, s, dev, st, fn);
+  constexpr int64_t per = kBlock * kAdamUnroll;
+  const int64_t groups = (n + 3) / 4;  // the last one may be partial
+  const int64_t blocks = (groups + per - 1) / per;
+  if (gdt == ZERO_BF16) {
+    hipLaunchKernelGGL((adamw_vec_kernel<ZERO_BF16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                       st, g, master_dev, m_dev, v_dev, param_dev, n, s, dev);
+  } else {
+    hipLaunchKernelGGL((adamw_vec_kernel<ZERO_FP16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
+                       st, g, master_dev, m_dev, v_dev, param_dev, n, s, dev);
+  }
+  return launch_status(fn);
+}
+
+int launch_adamw_tiled(const char* fn, const void* grad_dev, int gdt, float* state_dev, uint16_t* param_dev, int64_t n,
+                       const AdamScalars& s, const zero_step_state* dev, hipStream_t st) {
+  if (n > 0 && !state_dev) return fail(ZERO_ERR_INVALID, "%s: NULL state", fn);
+  if (!aligned16(state_dev)) return fail(ZERO_ERR_INVALID, "%s: state must be 16-byte aligned", fn);
+  if (n == 0) return ZERO_OK;
+  const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
+  if (!aligned8(grad_dev) || !aligned8(param_dev))
+    return launch_elements<true>(g, gdt, state_dev, state_dev, state_dev, param_dev, 0, n, s, dev, st, fn);
+  const int64_t tiles = (n + kTile - 1) / kTile;
+  auto* state = reinterpret_cast<f32x4*>(state_dev);
+  if (gdt == ZERO_BF16) {
+    hipLaunchKernelGGL(adamw_tiled_kernel<ZERO_BF16>, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, st, g,
+                       state, param_dev, n, s, dev);
+  } else {
+    hipLaunchKernelGGL(adamw_tiled_kernel<ZERO_FP16>, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, st, g,
+                       state, param_dev, n, s, dev);
+  }
+  return launch_status(fn);
+}
+
+int dev_args_ok(const char* fn, const void* grad_dev, int gdt, const void* param_dev, int64_t n,
+                const zero_step_state* dev) {
+  if (!dtype_ok(gdt)) return fail(ZERO_ERR_INVALID, "%s: unknown dtype %d", fn, gdt);
+  if (!dev || !aligned16(dev)) return fail(ZERO_ERR_INVALID, "%s: step state NULL or not 16-byte aligned", fn);
+  if (n < 0) return fail(ZERO_ERR_INVALID, "%s: n < 0", fn);
+  if (n > 0 && (!grad_dev || !param_dev)) return fail(ZERO_ERR_INVALID, "%s: NULL grad or param", fn);
+  if (((reinterpret_cast<uintptr_t>(grad_dev) | reinterpret_cast<uintptr_t>(param_dev)) & 1u) != 0)
+    return fail(ZERO_ERR_INVALID, "%s: 16-bit buffers not 2-byte aligned", fn);
+  return ZERO_OK;
+}
+
+__global__ void step_state_init_kernel(zero_step_state* st, double loss_scale, int32_t growth_interval) {
+  if (threadIdx.x != 0) return;
+  st->loss_scale = loss_scale;
+  st->global_norm = 0.0;
+  st->grad_scale = 0.0;
+  st->adam_step = 0;
+  st->iteration = 0;
+  st->good_steps = 0;
+  st->growth_interval = growth_interval;
+  st->skip = 1;  // nothing decided yet: an update launched now does nothing
+  st->reserved = 0;
+  for (int k = 0; k < 12; ++k) st->scalars[k] = 0.0f;
+}
+
+// The host decision (zero_step_decision) and scalar derivation (adam_args_ok)
+// on one thread, operation for operation.
+__global__ void step_decision_kernel(const double* __restrict__ sq, const int32_t* __restrict__ flags, int32_t n_ranks,
+                                     double max_norm, double lr, double beta1, double beta2, double eps, double wd,
+                                     zero_step_state* __restrict__ st) {
+  if (threadIdx.x != 0) return;
+  double global = 0.0;
+  bool overflow = false;
+  for (int32_t r = 0; r < n_ranks; ++r) {
+    global += sq[r];
+    overflow = overflow || flags[r] != 0;
+  }
+  const double scale = st->loss_scale;
+  st->iteration += 1;
+  if (overflow) {
+    st->skip = 1;
+    st->grad_scale = 0.0;
+    st->global_norm = __builtin_nan("");
+    st->loss_scale = scale * 0.5;
+    st->good_steps = 0;
+    return;
+  }
+  const double unscaled = global / (scale * scale);
+  double coef = 1.0;
+  if (max_norm > 0.0) {
+    const double c = max_norm / (sqrt(unscaled) + 1e-6);
+    coef = c < 1.0 ? c : 1.0;
+  }
+  const double gscale = coef / scale;
+  int32_t good = st->good_steps + 1;
+  double new_scale = scale;
+  if (good >= st->growth_interval) {
+    new_scale = scale * 2.0;
+    good = 0;
+  }
+  const int64_t t = st->adam_step + 1;
+  const double bc1 = 1.0 - pow(beta1, static_cast<double>(t));
+  const double bc2 = 1.0 - pow(beta2, static_cast<double>(t));
+  st->skip = 0;
+  st->grad_scale = gscale;
+  st->global_norm = sqrt(unscaled);
+  st->loss_scale = new_scale;
+  st->good_steps = good;
+  st->adam_step = t;
+  st->scalars[0] = static_cast<float>(beta1);
+  st->scalars[1] = static_cast<float>(1.0 - beta1);
+  st->scalars[2] = static_cast<float>(beta2);
+  st->scalars[3] = static_cast<float>(1.0 - beta2);
+  st->scalars[4] = static_cast<float>(eps);
+  st->scalars[5] = static_cast<float>(1.0 - lr * wd);
+  st->scalars[6] = static_cast<float>(lr / bc1);
+  st->scalars[7] = static_cast<float>(sqrt(bc2));
+  st->scalars[8] = static_cast<float>(gscale);
 }
 
 int flatten_args_ok(const char* fn, const zero_flat_seg* segs_dev, int32_t n_segs, int dt, const void* shard_dev,
@@ -781,29 +956,16 @@ int zero_adamw_step(const void* grad_dev, zero_dtype gdt, float* master_dev, flo
   AdamScalars s;
   int rc = adam_args_ok("zero_adamw_step", grad_dev, gdt, param_dev, n, hp, &s);
   if (rc != ZERO_OK) return rc;
-  if (n > 0 && (!master_dev || !m_dev || !v_dev)) return fail(ZERO_ERR_INVALID, "zero_adamw_step: NULL state");
-  if (((reinterpret_cast<uintptr_t>(master_dev) | reinterpret_cast<uintptr_t>(m_dev) |
-        reinterpret_cast<uintptr_t>(v_dev)) & 3u) != 0)
-    return fail(ZERO_ERR_INVALID, "zero_adamw_step: fp32 buffers not 4-byte aligned");
-  if (n == 0) return ZERO_OK;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool vec = aligned8(grad_dev) && aligned8(param_dev) && aligned16(master_dev) && aligned16(m_dev) &&
-                   aligned16(v_dev);
-  if (!vec)
-    return launch_elements<false>(static_cast<const uint16_t*>(grad_dev), gdt, master_dev, m_dev, v_dev, param_dev,
-                                  0, n, s, st, "zero_adamw_step (elements)");
-  constexpr int64_t per = kBlock * kAdamUnroll;
-  const int64_t groups = (n + 3) / 4;  // the last one may be partial
-  const int64_t blocks = (groups + per - 1) / per;
-  const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
-  if (gdt == ZERO_BF16) {
-    hipLaunchKernelGGL((adamw_vec_kernel<ZERO_BF16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                       st, g, master_dev, m_dev, v_dev, param_dev, n, s);
-  } else {
-    hipLaunchKernelGGL((adamw_vec_kernel<ZERO_FP16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                       st, g, master_dev, m_dev, v_dev, param_dev, n, s);
-  }
-  return launch_status("zero_adamw_step");
+  return launch_adamw_arrays("zero_adamw_step", grad_dev, gdt, master_dev, m_dev, v_dev, param_dev, n, s, nullptr,
+                             static_cast<hipStream_t>(stream));
+}
+
+int zero_adamw_step_dev(const void* grad_dev, zero_dtype gdt, float* master_dev, float* m_dev, float* v_dev,
+                        uint16_t* param_dev, int64_t n, const zero_step_state* state_dev, void* stream) {
+  int rc = dev_args_ok("zero_adamw_step_dev", grad_dev, gdt, param_dev, n, state_dev);
+  if (rc != ZERO_OK) return rc;
+  return launch_adamw_arrays("zero_adamw_step_dev", grad_dev, gdt, master_dev, m_dev, v_dev, param_dev, n,
+                             AdamScalars{}, state_dev, static_cast<hipStream_t>(stream));
 }
 
 int64_t zero_state_tiled_numel(int64_t n) {
@@ -816,24 +978,37 @@ int zero_adamw_step_tiled(const void* grad_dev, zero_dtype gdt, float* state_dev
   AdamScalars s;
   int rc = adam_args_ok("zero_adamw_step_tiled", grad_dev, gdt, param_dev, n, hp, &s);
   if (rc != ZERO_OK) return rc;
-  if (n > 0 && !state_dev) return fail(ZERO_ERR_INVALID, "zero_adamw_step_tiled: NULL state");
-  if (!aligned16(state_dev)) return fail(ZERO_ERR_INVALID, "zero_adamw_step_tiled: state must be 16-byte aligned");
-  if (n == 0) return ZERO_OK;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
-  if (!aligned8(grad_dev) || !aligned8(param_dev))
-    return launch_elements<true>(g, gdt, state_dev, state_dev, state_dev, param_dev, 0, n, s, st,
-                                 "zero_adamw_step_tiled (elements)");
-  const int64_t tiles = (n + kTile - 1) / kTile;
-  auto* state = reinterpret_cast<f32x4*>(state_dev);
-  if (gdt == ZERO_BF16) {
-    hipLaunchKernelGGL(adamw_tiled_kernel<ZERO_BF16>, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, st, g,
-                       state, param_dev, n, s);
-  } else {
-    hipLaunchKernelGGL(adamw_tiled_kernel<ZERO_FP16>, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, st, g,
-                       state, param_dev, n, s);
-  }
-  return launch_status("zero_adamw_step_tiled");
+  return launch_adamw_tiled("zero_adamw_step_tiled", grad_dev, gdt, state_dev, param_dev, n, s, nullptr,
+                            static_cast<hipStream_t>(stream));
+}
+
+int zero_adamw_step_tiled_dev(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev, int64_t n,
+                              const zero_step_state* step_state_dev, void* stream) {
+  int rc = dev_args_ok("zero_adamw_step_tiled_dev", grad_dev, gdt, param_dev, n, step_state_dev);
+  if (rc != ZERO_OK) return rc;
+  return launch_adamw_tiled("zero_adamw_step_tiled_dev", grad_dev, gdt, state_dev, param_dev, n, AdamScalars{},
+                            step_state_dev, static_cast<hipStream_t>(stream));
+}
+
+int zero_step_state_init(zero_step_state* state_dev, double loss_scale, int32_t growth_interval, void* stream) {
+  if (!state_dev || !aligned16(state_dev) || !(loss_scale > 0.0) || !std::isfinite(loss_scale) || growth_interval < 1)
+    return fail(ZERO_ERR_INVALID, "zero_step_state_init: bad arguments");
+  hipLaunchKernelGGL(step_state_init_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), state_dev,
+                     loss_scale, growth_interval);
+  return launch_status("zero_step_state_init");
+}
+
+int zero_step_decision_dev(const double* rank_sqnorms_dev, const int32_t* rank_flags_dev, int32_t n_ranks,
+                           double max_norm, const zero_adamw_hparams* hp, zero_step_state* state_dev, void* stream) {
+  if (n_ranks < 1 || !rank_sqnorms_dev || !rank_flags_dev || !hp || !state_dev || !aligned16(state_dev))
+    return fail(ZERO_ERR_INVALID, "zero_step_decision_dev: bad arguments");
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) || !(hp->eps >= 0.0) ||
+      !(hp->lr >= 0.0) || !std::isfinite(hp->lr) || !(hp->weight_decay >= 0.0))
+    return fail(ZERO_ERR_INVALID, "zero_step_decision_dev: hyper-parameters out of range");
+  hipLaunchKernelGGL(step_decision_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), rank_sqnorms_dev,
+                     rank_flags_dev, n_ranks, max_norm, hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay,
+                     state_dev);
+  return launch_status("zero_step_decision_dev");
 }
 
 int zero_state_tile(const float* master_dev, const float* m_dev, const float* v_dev, float* state_dev, int64_t n,

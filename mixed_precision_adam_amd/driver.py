@@ -13,9 +13,11 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import (ZERO_BF16, ZERO_FP16, ZERO_STATE_TILE, zero_adamw_step, zero_adamw_step_tiled, zero_flatten_grads,
-               zero_flatten_grads_sqnorm, zero_flatten_plan, zero_grad_sqnorm, zero_grad_sqnorm_workspace_bytes,
-               zero_shard_layout, zero_state_tile, zero_state_tiled_numel, zero_state_untile, zero_step_decision)
+from . import (ZERO_BF16, ZERO_FP16, ZERO_STATE_TILE, read_step_state, zero_adamw_step, zero_adamw_step_dev,
+               zero_adamw_step_tiled, zero_adamw_step_tiled_dev, zero_flatten_grads, zero_flatten_grads_sqnorm,
+               zero_flatten_plan, zero_grad_sqnorm, zero_grad_sqnorm_workspace_bytes, zero_shard_layout,
+               zero_state_tile, zero_state_tiled_numel, zero_state_untile, zero_step_decision, zero_step_decision_dev,
+               zero_step_state_init)
 
 _TORCH16 = {ZERO_BF16: torch.bfloat16, ZERO_FP16: torch.float16}
 
@@ -137,6 +139,14 @@ class RankShard:
         """Host copies of the last sqnorm; call after the stream has been synchronized."""
         return float(self._norm_np[0]), int(self._norm_np[1:2].view(np.int32)[0])
 
+    def adamw_dev(self, step_state, stream=None) -> None:
+        """The update with its scalars taken from a device-resident zero_step_state."""
+        if self.tiled:
+            zero_adamw_step_tiled_dev(self.grad, self.grad_dtype, self.state, self.param, self.n, step_state, stream)
+        else:
+            zero_adamw_step_dev(self.grad, self.grad_dtype, self.master, self.m, self.v, self.param, self.n,
+                                step_state, stream)
+
     def adamw(self, cfg: AdamWConfig, grad_scale: float, step: int, stream=None) -> None:
         kw = dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, weight_decay=cfg.weight_decay,
                   grad_scale=grad_scale, step=step, stream=stream)
@@ -144,6 +154,44 @@ class RankShard:
             zero_adamw_step_tiled(self.grad, self.grad_dtype, self.state, self.param, self.n, **kw)
         else:
             zero_adamw_step(self.grad, self.grad_dtype, self.master, self.m, self.v, self.param, self.n, **kw)
+
+
+class DeviceDecision:
+    """Device-resident decision for a set of simulated ranks: their square-norms and flags land side by side
+    in one device buffer, one GPU thread takes the decision, and the update kernels read it from device
+    memory.  A step then needs no host round trip (and can be captured in a HIP graph)."""
+
+    def __init__(self, shards, cfg: AdamWConfig, loss_scale: float = 1.0, growth_interval: int = 2**31 - 1):
+        n = len(shards)
+        dev = shards[0].device
+        self.shards = shards
+        self.cfg = cfg
+        self.norms = torch.zeros(n + (n + 1) // 2, dtype=torch.float64, device=dev)  # n doubles, then n int32
+        self.sq_base = self.norms.data_ptr()
+        self.flag_base = self.sq_base + 8 * n
+        for r, sh in enumerate(shards):
+            sh.sq_dev = self.sq_base + 8 * r
+            sh.flag_dev = self.flag_base + 4 * r
+        self.state = torch.zeros(16, dtype=torch.float64, device=dev)  # 128 bytes >= sizeof(zero_step_state)
+        zero_step_state_init(self.state, loss_scale, growth_interval)
+
+    def step(self, flatten: bool = True, stream=None) -> None:
+        """Enqueues one whole step; nothing waits on the host."""
+        stream = stream or torch.cuda.current_stream()
+        for sh in self.shards:
+            if flatten:
+                sh.flatten(stream)
+            if not (flatten and sh.fused):
+                sh.sqnorm(stream)
+        c = self.cfg
+        zero_step_decision_dev(self.sq_base, self.flag_base, len(self.shards), c.max_norm, self.state, lr=c.lr,
+                               beta1=c.beta1, beta2=c.beta2, eps=c.eps, weight_decay=c.weight_decay, stream=stream)
+        for sh in self.shards:
+            sh.adamw_dev(self.state, stream)
+
+    def read(self) -> dict:
+        """The decided state (synchronizes)."""
+        return read_step_state(self.state)
 
 
 def wait_spin(stream) -> None:

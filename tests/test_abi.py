@@ -148,10 +148,12 @@ def test_single_hip_runtime():
 
 
 def test_tiled_numel_and_invalid_tiled_args():
+    T = Z.ZERO_STATE_TILE
+    assert T == 1024
     assert Z.zero_state_tiled_numel(0) == 0
-    assert Z.zero_state_tiled_numel(1) == 3 * 1024
-    assert Z.zero_state_tiled_numel(1024) == 3 * 1024
-    assert Z.zero_state_tiled_numel(1025) == 6 * 1024
+    assert Z.zero_state_tiled_numel(1) == 3 * T
+    assert Z.zero_state_tiled_numel(T) == 3 * T
+    assert Z.zero_state_tiled_numel(T + 1) == 6 * T
     lib = Z.library()
     hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 1)
     assert lib.zero_adamw_step_tiled(16, 0, 24, 16, 8, hp, None) == Z.ZERO_ERR_INVALID  # state not 16-B aligned

@@ -32,7 +32,7 @@ if torch.cuda.is_available():
     from mixed_precision_adam_amd.driver import AdamWConfig, RankShard, ScalerState, rank_norms, rank_update
 
 WIN = 65536
-TILE = 1024
+TILE = 1024  # ZERO_STATE_TILE: windows start on tile boundaries
 
 
 def windows(layout, segments):

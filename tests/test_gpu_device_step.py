@@ -1,0 +1,194 @@
+"""The device-resident decision: one GPU thread repeats the host decision and
+scalar derivation, the update kernels read them from device memory, and a
+whole step can be captured in a HIP graph."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.workloads import WORKLOADS
+from tests.parity import (assert_bf16_within_ulp, assert_bits_equal, assert_f32_close, assert_grad_scale_close,
+                          assert_norm_close)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import mixed_precision_adam_amd as Z
+    from mixed_precision_adam_amd.driver import AdamWConfig, DeviceDecision, RankShard
+
+DEV = "cuda:0"
+
+
+def _f32bits(x):
+    return np.array([x], dtype=np.float32).view(np.uint32)[0]
+
+
+def test_decision_kernel_matches_host_decision():
+    rng = np.random.default_rng(2024)
+    state = torch.zeros(16, dtype=torch.float64, device=DEV)
+    for trial in range(40):
+        n = int(rng.integers(1, 6))
+        scale = float(2.0 ** rng.integers(0, 17))
+        growth = int(rng.choice([1, 2, 3, 1000]))
+        hp = dict(lr=float(rng.choice([0.0, 1e-4, 3e-3, 0.05])), beta1=float(rng.choice([0.0, 0.8, 0.9, 0.99])),
+                  beta2=float(rng.choice([0.0, 0.95, 0.999, 0.9999])), eps=float(rng.choice([1e-8, 1e-3])),
+                  weight_decay=float(rng.choice([0.0, 0.01, 0.1])))
+        max_norm = float(rng.choice([0.0, 0.5, 1.0, 5.0]))
+        Z.zero_step_state_init(state, scale, growth)
+        h_scale, h_good, h_t = scale, 0, 0
+        for it in range(12):
+            sq = rng.random(n) * 10.0 ** rng.uniform(-4, 6) * scale * scale
+            fl = (rng.random(n) < 0.15).astype(np.int32)
+            buf = torch.zeros(n + (n + 1) // 2, dtype=torch.float64, device=DEV)
+            buf[:n] = torch.from_numpy(sq)
+            buf.view(torch.int32)[2 * n: 3 * n] = torch.from_numpy(fl)
+            Z.zero_step_decision_dev(buf.data_ptr(), buf.data_ptr() + 8 * n, n, max_norm, state, **hp)
+            got = Z.read_step_state(state)
+            host = Z.zero_step_decision(list(sq), list(fl), max_norm, h_scale, h_good, growth)
+            h_scale, h_good = host["loss_scale"], host["good_steps"]
+            what = f"trial {trial} it {it}"
+            assert got["skip"] == host["skip"], what
+            assert got["loss_scale"] == host["loss_scale"] and got["good_steps"] == host["good_steps"], what
+            assert got["iteration"] == it + 1, what
+            if host["skip"]:
+                assert math.isnan(got["global_norm"]) and got["grad_scale"] == 0.0, what
+                assert got["adam_step"] == h_t, what
+                continue
+            h_t += 1
+            assert got["adam_step"] == h_t, what
+            assert got["grad_scale"] == host["grad_scale"], (what, got["grad_scale"], host["grad_scale"])
+            assert got["global_norm"] == host["global_norm"], what
+            ref = oracle.adamw_scalars(grad_scale=host["grad_scale"], step=h_t, **hp)
+            names = ["b1", "omb1", "b2", "omb2", "eps", "decay", "step_size", "bc2_sqrt", "gscale"]
+            for k, name in enumerate(names):
+                assert _f32bits(got["scalars"][k]) == ref[name].view(np.uint32), (what, name)
+
+
+def test_update_skips_when_decision_says_so():
+    n = 5000
+    p = torch.randn(n, device=DEV)
+    m, v = torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    q = torch.full((n,), 3.0, dtype=torch.bfloat16, device=DEV)
+    g = torch.randn(n, device=DEV).to(torch.bfloat16)
+    state = torch.zeros(16, dtype=torch.float64, device=DEV)
+    Z.zero_step_state_init(state, 1.0, 1000)  # nothing decided yet: skip
+    p0 = p.clone()
+    Z.zero_adamw_step_dev(g, 0, p, m, v, q, n, state)
+    tiled = torch.zeros(Z.zero_state_tiled_numel(n), device=DEV)
+    Z.zero_adamw_step_tiled_dev(g, 0, tiled, q, n, state)
+    torch.cuda.synchronize()
+    assert torch.equal(p, p0) and (m == 0).all() and (q == 3.0).all() and (tiled == 0).all()
+
+
+def _setup(w, tiled=True, fused=True):
+    dev = torch.device(DEV)
+    src = torch.empty(w.psi, dtype=torch.bfloat16 if w.grad_kind == synth.BF16 else torch.float16, device=dev)
+    gdt = Z.ZERO_BF16 if w.grad_kind == synth.BF16 else Z.ZERO_FP16
+    shards = [RankShard(w.numels, w.world, r, gdt, dev, sources=[src], tiled=tiled, fused=fused) for r in w.ranks]
+    master_all = synth.fill_host(w.master_field(), 0, w.psi)
+    for sh in shards:
+        lay = sh.layout
+        p = np.zeros(sh.n, np.float32)
+        p[:lay.shard_valid] = master_all[lay.shard_offset:lay.shard_offset + lay.shard_valid]
+        sh.load_master(torch.from_numpy(p).to(dev))
+    return src, shards, master_all
+
+
+@pytest.mark.parametrize("tiled", [True, False])
+def test_device_step_tiny_against_oracle(tiled):
+    w = WORKLOADS["tiny"]
+    src, shards, master_all = _setup(w, tiled=tiled)
+    cfg = AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, max_norm=w.clip)
+    dd = DeviceDecision(shards, cfg)
+    s = shards[0].n
+    refs = []
+    for sh in shards:
+        lay = sh.layout
+        p = np.zeros(s, np.float32)
+        p[:lay.shard_valid] = master_all[lay.shard_offset:lay.shard_offset + lay.shard_valid]
+        refs.append([p, np.zeros(s, np.float32), np.zeros(s, np.float32), np.zeros(s, np.uint16)])
+    oscale, ogood = 1.0, 0
+    for t in range(1, w.steps + 1):
+        synth.fill_tensor(w.grad_field(t), 0, src)
+        dd.step()
+        got = dd.read()
+        flat = synth.fill_host(w.grad_field(t), 0, w.psi)
+        grads = [oracle.flatten([flat], w.numels, w.world, r) for r in w.ranks]
+        norms = [oracle.sqnorm(g, 0) for g in grads]
+        od = oracle.step_decision([x[0] for x in norms], [x[1] for x in norms], w.clip, oscale, ogood, 2**31 - 1)
+        oscale, ogood = od["loss_scale"], od["good_steps"]
+        assert got["skip"] == 0 and got["adam_step"] == t
+        same = assert_grad_scale_close(got["grad_scale"], od["grad_scale"], w.world * s, f"step {t}")
+        for r, sh in enumerate(shards):
+            p, m, v, q = refs[r]
+            oracle.adamw_step(grads[r], 0, p, m, v, q, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                              weight_decay=w.weight_decay, grad_scale=od["grad_scale"], step=t)
+            gp, gm, gv = (x.cpu().numpy() for x in sh.read_state())
+            what = f"step {t} rank {r}"
+            nd = assert_f32_close(gp, p, what + " master") + assert_f32_close(gm, m, what + " m")
+            nd += assert_f32_close(gv, v, what + " v")
+            nd += assert_bf16_within_ulp(sh.param.view(torch.int16).cpu().numpy().view(np.uint16), q, what)
+            assert nd == 0 or not same, what
+
+
+def test_device_step_skips_overflow_and_halves_scale():
+    w = WORKLOADS["tiny"]
+    w16 = type(w)(**{**w.__dict__, "grad_kind": synth.FP16, "loss_scale": 1024.0, "ranks": [0, 1, 2, 3]})
+    src, shards, _ = _setup(w16)
+    cfg = AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, max_norm=w.clip)
+    dd = DeviceDecision(shards, cfg, loss_scale=1024.0, growth_interval=1000)
+    synth.fill_tensor(w16.grad_field(1, 1024.0), 0, src)
+    dd.step()
+    st1 = dd.read()
+    assert st1["skip"] == 0 and st1["adam_step"] == 1
+    before = [tuple(x.clone() for x in sh.read_state()) + (sh.param.clone(),) for sh in shards]
+    synth.fill_tensor(w16.grad_field(2, 1024.0), 0, src)
+    src.view(torch.int16)[777_777] = 0x7C00  # +inf lands in rank 3's shard
+    dd.step()
+    st2 = dd.read()
+    assert st2["skip"] == 1 and st2["adam_step"] == 1 and st2["loss_scale"] == 512.0 and st2["iteration"] == 2
+    for sh, b in zip(shards, before):
+        after = sh.read_state() + (sh.param,)
+        for x, y in zip(after, b):
+            assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                               y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+    synth.fill_tensor(w16.grad_field(3, 512.0), 0, src)
+    dd.step()
+    st3 = dd.read()
+    assert st3["skip"] == 0 and st3["adam_step"] == 2 and st3["loss_scale"] == 512.0
+
+
+def test_whole_step_captured_in_a_graph():
+    """Two identical rank sets: one stepped eagerly, one by replaying a captured HIP graph of the whole step
+    (flatten+norm, decision, update).  Fresh gradients are written eagerly between replays, with host
+    synchronisation in between; every replay must match the eager step bit for bit."""
+    w = WORKLOADS["tiny"]
+    cfg = AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, max_norm=w.clip)
+    src_a, shards_a, _ = _setup(w)
+    src_b, shards_b, _ = _setup(w)
+    dd_a = DeviceDecision(shards_a, cfg)
+    dd_b = DeviceDecision(shards_b, cfg)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dd_b.step()
+    # capture recorded the work without running it: the states are still the initial ones
+    Z.zero_step_state_init(dd_b.state, 1.0, 2**31 - 1)
+    torch.cuda.synchronize()
+    for t in range(1, 5):
+        synth.fill_tensor(w.grad_field(t), 0, src_a)
+        synth.fill_tensor(w.grad_field(t), 0, src_b)
+        torch.cuda.synchronize()
+        dd_a.step()
+        graph.replay()
+        torch.cuda.synchronize()
+        sa, sb = dd_a.read(), dd_b.read()
+        assert sa == sb, (t, sa, sb)
+        assert sa["adam_step"] == t
+        for a, b in zip(shards_a, shards_b):
+            assert torch.equal(a.state.view(torch.int32), b.state.view(torch.int32)), t
+            assert torch.equal(a.param.view(torch.int16), b.param.view(torch.int16)), t
+            assert torch.equal(a.grad.view(torch.int16), b.grad.view(torch.int16)), t

@@ -323,12 +323,13 @@ def _tiled_case(n, dt, gq_offset, hp, steps, seed):
     check_guards(sbuf, 0, tn, "tiled state")
     check_guards(qbuf, gq_offset, n, "tiled param")
     # padding floats of the last tile are never written
-    if n % 1024:
-        tail = state.view(-1, 3, 1024)[-1][:, n % 1024:]
+    T = Z.ZERO_STATE_TILE
+    if n % T:
+        tail = state.view(-1, 3, T)[-1][:, n % T:]
         assert (tail == 0).all()
 
 
-@pytest.mark.parametrize("n", [1, 5, 1023, 1024, 1025, 4096 * 3 + 7, 100_003])
+@pytest.mark.parametrize("n", [1, 5, 1023, 1024, 1025, 2047, 2048, 2049, 2048 + 1027, 4096 * 3 + 7, 100_003])
 @pytest.mark.parametrize("dt", [0, 1])
 def test_adamw_tiled_sizes(n, dt):
     _tiled_case(n, dt, 0, HP_SETS[0], 2, n + 7 * dt)
@@ -336,7 +337,7 @@ def test_adamw_tiled_sizes(n, dt):
 
 @pytest.mark.parametrize("off", [1, 2, 4])
 def test_adamw_tiled_unaligned_grad_param(off):
-    _tiled_case(5 * 1024 + 3, 0, off, HP_SETS[1], 2, off)
+    _tiled_case(5 * Z.ZERO_STATE_TILE + 3, 0, off, HP_SETS[1], 2, off)
 
 
 def test_tiled_matches_separate_arrays_bitwise():
@@ -362,7 +363,8 @@ def test_tiled_matches_separate_arrays_bitwise():
 
 
 def test_tile_untile_roundtrip():
-    for n in (1, 1000, 1024, 2049, 77_777):
+    T = Z.ZERO_STATE_TILE
+    for n in (1, 1000, 1024, 2048, 2049, 4097, 77_777):
         src = [torch.randn(n, device=DEV) for _ in range(3)]
         state = torch.full((Z.zero_state_tiled_numel(n),), 7.0, device=DEV)
         Z.zero_state_tile(*src, state, n)
@@ -371,8 +373,8 @@ def test_tile_untile_roundtrip():
         torch.cuda.synchronize()
         for a, b in zip(src, back):
             assert torch.equal(a.view(torch.int32), b.view(torch.int32))
-        tiles = state.view(-1, 3, 1024)
+        tiles = state.view(-1, 3, T)
         assert torch.equal(tiles[:, 0, :].reshape(-1)[:n], src[0])
         assert torch.equal(tiles[:, 2, :].reshape(-1)[:n], src[2])
-        if n % 1024:
-            assert (tiles[-1][:, n % 1024:] == 7.0).all()
+        if n % T:
+            assert (tiles[-1][:, n % T:] == 7.0).all()
