@@ -430,7 +430,10 @@ __global__ __launch_bounds__(kBlock) void sqnorm_final_kernel(const double* __re
 // A workgroup copies len 16-bit elements from s to d.  When both addresses
 // share their position inside a 16-byte line, a scalar head brings d to a
 // 16-byte boundary and the body moves 16-byte vectors.  With ACC the copied
-// values are also squared into acc (fp64) and checked for inf/NaN.
+// values are also squared into acc (fp64) and checked for inf/NaN.  Source
+// reads stream (non-temporal); the shard is stored with ordinary stores: the
+// update reads it back right away, and on MI355X the whole step is 1.4%
+// faster that way (the flatten itself 15%).
 // Source tensors are plain device allocations (global memory); saying so lets
 // the compiler use global rather than flat loads for them.
 typedef const u32x4 __attribute__((address_space(1)))* global_u32x4_ptr;
@@ -461,7 +464,7 @@ __device__ void copy_piece(const uint16_t* __restrict__ s_generic, uint16_t* __r
 #pragma unroll
     for (int u = 0; u < kU; ++u) w[u] = __builtin_nontemporal_load(sv + j + u * kBlock);
 #pragma unroll
-    for (int u = 0; u < kU; ++u) st_stream(dv + j + u * kBlock, w[u]);
+    for (int u = 0; u < kU; ++u) dv[j + u * kBlock] = w[u];
     if (ACC) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) accumulate8<DT>(w[u], acc, bad);
@@ -469,7 +472,7 @@ __device__ void copy_piece(const uint16_t* __restrict__ s_generic, uint16_t* __r
   }
   for (; j < nv; j += kBlock) {
     const u32x4 w = __builtin_nontemporal_load(sv + j);
-    st_stream(dv + j, w);
+    dv[j] = w;
     if (ACC) accumulate8<DT>(w, acc, bad);
   }
   for (int64_t t = head + 8 * nv + threadIdx.x; t < len; t += kBlock) {
