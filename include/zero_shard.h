@@ -76,6 +76,16 @@ typedef struct zero_layout {
   int64_t bytes_zero1;  /* 2·N·S + 2·N·S + 12·S */
   int64_t bytes_zero2;  /* 2·N·S + 14·S */
   int64_t bytes_zero3;  /* 16·S */
+  /* Elements this rank sends per training step with ring collectives over the
+   * padded flat space ([Z] section 六: a ring reduce-scatter or all-gather of
+   * N·S elements sends (N-1)·S per rank; DP all-reduces the gradients (RS +
+   * AG); ZeRO-1/2 reduce-scatter the gradients and all-gather the updated
+   * parameters; ZeRO-3 also all-gathers the parameters once more, once for
+   * forward and once for backward).  Multiply by the element size for bytes. */
+  int64_t comm_dp;      /* 2·(N-1)·S */
+  int64_t comm_zero1;   /* 2·(N-1)·S */
+  int64_t comm_zero2;   /* 2·(N-1)·S */
+  int64_t comm_zero3;   /* 3·(N-1)·S */
 } zero_layout;
 
 /* One piece of a tensor that lands in the shard. */

@@ -48,7 +48,8 @@ class zero_layout(C.Structure):
     _fields_ = [("psi", C.c_int64), ("padded_numel", C.c_int64), ("shard_numel", C.c_int64),
                 ("shard_offset", C.c_int64), ("shard_valid", C.c_int64), ("world", C.c_int32), ("rank", C.c_int32),
                 ("bytes_dp", C.c_int64), ("bytes_zero1", C.c_int64), ("bytes_zero2", C.c_int64),
-                ("bytes_zero3", C.c_int64)]
+                ("bytes_zero3", C.c_int64), ("comm_dp", C.c_int64), ("comm_zero1", C.c_int64),
+                ("comm_zero2", C.c_int64), ("comm_zero3", C.c_int64)]
 
 
 class zero_segment(C.Structure):
@@ -158,6 +159,10 @@ class Layout:
     bytes_zero1: int
     bytes_zero2: int
     bytes_zero3: int
+    comm_dp: int
+    comm_zero1: int
+    comm_zero2: int
+    comm_zero3: int
 
 
 def zero_shard_layout(numels, world: int, rank: int):

@@ -786,6 +786,11 @@ int zero_shard_layout(const int64_t* numels, int32_t n_tensors, int32_t world, i
   L.bytes_zero1 = (2 + 2) * L.padded_numel + 12 * shard;   // optimizer state partitioned
   L.bytes_zero2 = 2 * L.padded_numel + (2 + 12) * shard;   // + gradients partitioned
   L.bytes_zero3 = (2 + 2 + 12) * shard;                    // + parameters partitioned
+  const int64_t ring = static_cast<int64_t>(world - 1) * shard;  // one ring RS or AG, sent per rank
+  L.comm_dp = 2 * ring;     // gradient all-reduce = RS + AG
+  L.comm_zero1 = 2 * ring;  // gradient RS + parameter AG
+  L.comm_zero2 = 2 * ring;
+  L.comm_zero3 = 3 * ring;  // + a second parameter AG (forward and backward each gather)
   *out = L;
 
   int32_t count = 0;

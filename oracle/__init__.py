@@ -43,6 +43,10 @@ class _Layout(C.Structure):
         ("bytes_zero1", C.c_int64),
         ("bytes_zero2", C.c_int64),
         ("bytes_zero3", C.c_int64),
+        ("comm_dp", C.c_int64),
+        ("comm_zero1", C.c_int64),
+        ("comm_zero2", C.c_int64),
+        ("comm_zero3", C.c_int64),
     ]
 
 
@@ -137,6 +141,10 @@ class Layout:
     bytes_zero1: int
     bytes_zero2: int
     bytes_zero3: int
+    comm_dp: int
+    comm_zero1: int
+    comm_zero2: int
+    comm_zero3: int
     segments: list  # list of (tensor, src_offset, dst_offset, numel)
 
 
@@ -156,7 +164,8 @@ def layout(numels, world: int, rank: int) -> Layout:
     _check(rc, "orc_layout_compute")
     seg_list = [(s.tensor, s.src_offset, s.dst_offset, s.numel) for s in segs[: n_segs.value]]
     return Layout(out.psi, out.padded_numel, out.shard_numel, out.shard_offset, out.shard_valid, out.world, out.rank,
-                  out.bytes_dp, out.bytes_zero1, out.bytes_zero2, out.bytes_zero3, seg_list)
+                  out.bytes_dp, out.bytes_zero1, out.bytes_zero2, out.bytes_zero3, out.comm_dp, out.comm_zero1,
+                  out.comm_zero2, out.comm_zero3, seg_list)
 
 
 def layout_status(numels, world: int, rank: int, cap: int):

@@ -108,6 +108,19 @@ int orc_layout_compute(const int64_t* numels, int32_t n_tensors, int32_t world, 
   out->bytes_zero2 = 2 * out->padded_numel + (2 + 12) * shard;
   out->bytes_zero3 = (2 + 2 + 12) * shard;
 
+  /* Communication per step ([Z] section 六): a ring reduce-scatter over N
+   * ranks takes N-1 rounds, each rank sending one 1/N chunk per round, and a
+   * ring all-gather the same; so each moves (N-1)/N of the (padded) flat
+   * space per rank.  Plain DP all-reduces the gradients (reduce-scatter +
+   * all-gather); ZeRO-1/2 reduce-scatter the gradients and all-gather the
+   * updated parameters; ZeRO-3 gathers the parameters for forward and again
+   * for backward and reduce-scatters the gradients. */
+  int64_t one_collective = (int64_t)(world - 1) * shard;
+  out->comm_dp = one_collective + one_collective;
+  out->comm_zero1 = one_collective + one_collective;
+  out->comm_zero2 = one_collective + one_collective;
+  out->comm_zero3 = one_collective + one_collective + one_collective;
+
   /* Tensors are laid end to end in list order; each contributes the part of
    * its flat range that falls inside [offset, offset + valid). */
   int32_t count = 0;

@@ -44,6 +44,7 @@ typedef struct {
   int64_t shard_valid;   /* elements of this shard below Ψ */
   int32_t world, rank;
   int64_t bytes_dp, bytes_zero1, bytes_zero2, bytes_zero3;
+  int64_t comm_dp, comm_zero1, comm_zero2, comm_zero3; /* elements sent per rank per step */
 } orc_layout;
 
 typedef struct {

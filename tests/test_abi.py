@@ -69,7 +69,7 @@ def _same_layout(numels, world, rank):
     lay, segs = Z.zero_shard_layout(numels, world, rank)
     ref = oracle.layout(numels, world, rank)
     for f in ("psi", "padded_numel", "shard_numel", "shard_offset", "shard_valid", "world", "rank", "bytes_dp",
-              "bytes_zero1", "bytes_zero2", "bytes_zero3"):
+              "bytes_zero1", "bytes_zero2", "bytes_zero3", "comm_dp", "comm_zero1", "comm_zero2", "comm_zero3"):
         assert getattr(lay, f) == getattr(ref, f), (f, numels, world, rank)
     assert [(s.tensor, s.src_offset, s.dst_offset, s.numel) for s in segs] == ref.segments
 

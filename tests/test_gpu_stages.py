@@ -1,0 +1,97 @@
+"""Stage equivalence on the GPU: ZeRO changes where model state lives and how
+gradients travel, not what a step computes ([D] 误区与复盘, second pitfall;
+[Z] section 四).  Three ways of running the same step on one GPU:
+
+  * ZeRO-2: each rank flattens its slice of the per-tensor gradients into its
+    own shard buffer (the reduce-scatter landing buffer) and updates it;
+  * ZeRO-1: gradients stay in one full all-reduced flat buffer and each rank's
+    norm and update read its slice of it directly, with no copy;
+  * plain DP: one rank (N = 1) updates everything.
+
+ZeRO-1 and ZeRO-2 must agree bit for bit (same bytes, same alignment, same
+kernels).  Gathering the N ranks' state must equal the DP state bit for bit
+whenever the two global norms give the same fp32 factor (several fp64
+summation orders are correct), and within tolerance otherwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests.parity import assert_f32_close, assert_grad_scale_close
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import mixed_precision_adam_amd as Z
+    from mixed_precision_adam_amd.driver import AdamWConfig, DeviceDecision, RankShard
+
+DEV = "cuda:0"
+NUMELS = [40_000, 1_600, 123_456, 8, 300_000, 97_432]  # Ψ = 562,496: N = 4 gives S = 140,624 = 8·17,578
+WORLD = 4
+SEED = 0x5EED0042
+
+
+def _field(t):
+    return synth.field(SEED, synth.STREAM_GRAD, t, 1e-3, synth.BF16)
+
+
+def _master_flat(psi):
+    m = torch.zeros(psi, device=DEV)
+    synth.fill_tensor(synth.field(SEED, synth.STREAM_MASTER, 0, 0.02, synth.F32), 0, m)
+    return m
+
+
+def test_zero1_zero2_and_dp_agree():
+    psi = sum(NUMELS)
+    lay0, _ = Z.zero_shard_layout(NUMELS, WORLD, 0)
+    s = lay0.shard_numel
+    assert s % 8 == 0 and WORLD * s == psi
+    cfg = AdamWConfig(lr=3e-3, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.1, max_norm=0.5)
+    offs = np.cumsum([0] + NUMELS)
+    master = _master_flat(psi)
+
+    # ZeRO-2: per-tensor sources, flatten (+ fused norm) into each rank's shard buffer
+    srcs = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for n in NUMELS]
+    z2 = [RankShard(NUMELS, WORLD, r, Z.ZERO_BF16, DEV, sources=srcs, tiled=True, fused=False) for r in range(WORLD)]
+    for r, sh in enumerate(z2):
+        sh.load_master(master[r * s:(r + 1) * s].contiguous())
+    d2 = DeviceDecision(z2, cfg)
+
+    # ZeRO-1: one full flat gradient buffer; each rank's grad *is* its slice (16-byte aligned: S % 8 == 0)
+    flat = torch.empty(psi, dtype=torch.bfloat16, device=DEV)
+    z1 = [RankShard(NUMELS, WORLD, r, Z.ZERO_BF16, DEV, tiled=True) for r in range(WORLD)]
+    for r, sh in enumerate(z1):
+        sh.grad = flat[r * s:(r + 1) * s]
+        sh.load_master(master[r * s:(r + 1) * s].contiguous())
+    d1 = DeviceDecision(z1, cfg)
+
+    # DP: a single rank over everything
+    dp = RankShard([psi], 1, 0, Z.ZERO_BF16, DEV, tiled=True)
+    dp.grad = flat
+    dp.load_master(master)
+    ddp = DeviceDecision([dp], cfg)
+
+    for t in range(1, 4):
+        f = _field(t)
+        for k, src in enumerate(srcs):
+            synth.fill_tensor(f, int(offs[k]), src)
+        synth.fill_tensor(f, 0, flat)
+        d2.step()                      # flatten + norm + decide + update
+        d1.step(flatten=False)         # norm of the slices + decide + update, no copy
+        ddp.step(flatten=False)
+        torch.cuda.synchronize()
+        s2, s1, sdp = d2.read(), d1.read(), ddp.read()
+        assert s1 == s2, (t, s1, s2)
+        for a, b in zip(z1, z2):
+            assert torch.equal(a.grad.view(torch.int16), b.grad.view(torch.int16))
+            assert torch.equal(a.state.view(torch.int32), b.state.view(torch.int32)), t
+            assert torch.equal(a.param.view(torch.int16), b.param.view(torch.int16)), t
+        same = assert_grad_scale_close(sdp["grad_scale"], s2["grad_scale"], psi, f"step {t} DP vs ZeRO")
+        gathered = [torch.cat([x for x in zip(*[sh.read_state() for sh in z2])][k]) for k in range(3)]
+        for k, name in enumerate(("master", "m", "v")):
+            nd = assert_f32_close(gathered[k].cpu().numpy(), dp.read_state()[k].cpu().numpy(), f"step {t} {name}")
+            assert nd == 0 or not same, (t, name, nd)
+        q = torch.cat([sh.param for sh in z2])
+        if same:
+            assert torch.equal(q.view(torch.int16), dp.param.view(torch.int16))

@@ -176,3 +176,27 @@ def test_error_paths():
     assert oracle.layout_status([-1], 2, 0, 4)[0] == -1
     rc, need = oracle.layout_status([1] * 8, 1, 0, 3)
     assert rc == -2 and need == 8
+
+
+def test_printed_communication_per_step():
+    """Per-rank elements sent per step with ring collectives ([Z] section 六; [X] section 五; operatorworld
+    通信账; golden file): 2Ψ / 2Ψ / 2Ψ / 3Ψ for large N, ZeRO-3 = 1.5 x DP, one ring collective (N-1)/N·Ψ."""
+    pins = PINS["comm_per_step"]
+    psi, n = 2**40, 2**20
+    lay = oracle.layout([psi], n, 0)
+    got = {"0": lay.comm_dp, "1": lay.comm_zero1, "2": lay.comm_zero2, "3": lay.comm_zero3}
+    for stage, mult in pins["printed_multiple_of_psi"].items():
+        assert abs(got[stage] / psi - mult) < 1e-5, (stage, got[stage] / psi)
+    for n in (2, 4, 8, 64, 1024):
+        lay = oracle.layout([n * 1000], n, 0)
+        assert lay.comm_zero3 * 2 == lay.comm_dp * 3  # exactly 1.5x
+        assert lay.comm_dp * n == 2 * (n - 1) * (n * 1000)  # 2·(N-1)/N·Ψ when N | Ψ
+    assert pins["printed_zero3_over_dp"] == 1.5
+
+
+def test_communication_eight_param_example():
+    """[Z] section 六（一）/（二）: 8 parameters on 4 GPUs; a ring reduce-scatter takes 3 rounds of a
+    2-element chunk, so each GPU sends 6 elements, and the all-gather another 6."""
+    lay = oracle.layout([8], 4, 2)
+    assert lay.comm_zero2 == 6 + 6 and lay.comm_dp == 12 and lay.comm_zero3 == 18
+    assert oracle.layout([8], 1, 0).comm_dp == 0  # one rank: nothing to exchange
