@@ -129,6 +129,19 @@ typedef struct zero_flat_seg {
 int zero_flatten_plan(const zero_segment* segs, int32_t n_segs, const void* const* tensor_ptrs, int32_t n_tensors,
                       zero_flat_seg* out);
 
+/* Host only.  Constant-capacity buckets of the shard ([Z] section 五（二）:
+ * fused buffers of a fixed capacity that does not grow with the model;
+ * section 四（二）: gradients are bucketed and reduced bucket by bucket as
+ * backward produces them).  Writes the parts of the layout's segments that
+ * fall in the shard window [win_begin, win_begin + win_numel), with
+ * dst_offset relative to the window, so that a bucket is flattened by
+ * zero_flatten_grads[_sqnorm] on shard + win_begin with shard_numel =
+ * win_numel.  Fills up to cap segments; *n_out receives the full count
+ * (ZERO_ERR_CAPACITY when it exceeds cap).  Elements of the window past the
+ * layout's shard_valid are padding (no segment covers them). */
+int zero_bucket_segments(const zero_segment* segs, int32_t n_segs, int64_t win_begin, int64_t win_numel,
+                         zero_segment* out, int32_t cap, int32_t* n_out);
+
 /* Device.  segs_dev: n_segs descriptors in device memory, sorted by
  * dst_offset and non-overlapping, each inside [0, shard_numel).  Writes
  * shard[0, shard_numel): covered elements are bit copies of the source,

@@ -74,6 +74,7 @@ _lib.zero_last_error.restype = C.c_char_p
 _lib.zero_shard_layout.argtypes = [_P, C.c_int32, C.c_int32, C.c_int32, C.POINTER(zero_layout), _P, C.c_int32,
                                    C.POINTER(C.c_int32)]
 _lib.zero_flatten_plan.argtypes = [_P, C.c_int32, _P, C.c_int32, _P]
+_lib.zero_bucket_segments.argtypes = [_P, C.c_int32, C.c_int64, C.c_int64, _P, C.c_int32, C.POINTER(C.c_int32)]
 _lib.zero_flatten_grads.argtypes = [_P, C.c_int32, C.c_int, _P, C.c_int64, _P]
 _lib.zero_grad_sqnorm_workspace_bytes.argtypes = [C.c_int64]
 _lib.zero_grad_sqnorm_workspace_bytes.restype = C.c_size_t
@@ -108,7 +109,7 @@ class zero_step_state(C.Structure):
                 ("scalars", C.c_float * 12)]
 
 # Every symbol include/zero_shard.h declares.
-EXPORTS = ("zero_last_error", "zero_shard_layout", "zero_flatten_plan", "zero_flatten_grads",
+EXPORTS = ("zero_last_error", "zero_shard_layout", "zero_flatten_plan", "zero_bucket_segments", "zero_flatten_grads",
            "zero_flatten_grads_sqnorm", "zero_grad_sqnorm_workspace_bytes", "zero_grad_sqnorm", "zero_step_decision",
            "zero_clip_coef", "zero_loss_scale_update", "zero_cosine_lr", "zero_adamw_step", "zero_state_tiled_numel",
            "zero_adamw_step_tiled", "zero_state_tile", "zero_state_untile", "zero_step_state_init",
@@ -178,6 +179,20 @@ def zero_shard_layout(numels, world: int, rank: int):
                                   n.value, C.byref(n)))
     lay = Layout(*(getattr(out, f) for f, _ in zero_layout._fields_))
     return lay, segs[:n.value]
+
+
+def zero_bucket_segments(segments, win_begin: int, win_numel: int):
+    """The layout segments that fall in shard window [win_begin, win_begin + win_numel), re-based to it."""
+    n = len(segments)
+    segs = (zero_segment * max(n, 1))(*segments)
+    cnt = C.c_int32(0)
+    st = _lib.zero_bucket_segments(C.cast(segs, _P), n, win_begin, win_numel, None, 0, C.byref(cnt))
+    if st not in (ZERO_OK, ZERO_ERR_CAPACITY):
+        _check(st)
+    out = (zero_segment * max(cnt.value, 1))()
+    _check(_lib.zero_bucket_segments(C.cast(segs, _P), n, win_begin, win_numel, C.cast(out, _P), cnt.value,
+                                     C.byref(cnt)))
+    return out[:cnt.value]
 
 
 def zero_flatten_plan(segments, tensor_ptrs) -> bytes:

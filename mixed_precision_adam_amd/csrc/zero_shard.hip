@@ -825,6 +825,27 @@ int zero_flatten_plan(const zero_segment* segs, int32_t n_segs, const void* cons
   return ZERO_OK;
 }
 
+int zero_bucket_segments(const zero_segment* segs, int32_t n_segs, int64_t win_begin, int64_t win_numel,
+                         zero_segment* out, int32_t cap, int32_t* n_out) {
+  if (n_segs < 0 || (n_segs > 0 && !segs) || win_begin < 0 || win_numel < 0 || cap < 0 || (cap > 0 && !out) ||
+      !n_out || win_numel > kMaxPsi - win_begin)
+    return fail(ZERO_ERR_INVALID, "zero_bucket_segments: bad arguments");
+  const int64_t win_end = win_begin + win_numel;
+  int32_t count = 0;
+  for (int32_t k = 0; k < n_segs; ++k) {
+    const zero_segment& sg = segs[k];
+    const int64_t a = sg.dst_offset > win_begin ? sg.dst_offset : win_begin;
+    const int64_t e = sg.dst_offset + sg.numel;
+    const int64_t b = e < win_end ? e : win_end;
+    if (b <= a) continue;
+    if (count < cap) out[count] = zero_segment{sg.tensor, 0, sg.src_offset + (a - sg.dst_offset), a - win_begin, b - a};
+    ++count;
+  }
+  *n_out = count;
+  if (count > cap) return fail(ZERO_ERR_CAPACITY, "zero_bucket_segments: %d segments needed, capacity %d", count, cap);
+  return ZERO_OK;
+}
+
 int zero_flatten_grads(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype dt, void* shard_dev,
                        int64_t shard_numel, void* stream) {
   int rc = flatten_args_ok("zero_flatten_grads", segs_dev, n_segs, dt, shard_dev, shard_numel);

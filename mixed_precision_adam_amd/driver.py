@@ -14,6 +14,7 @@ import numpy as np
 import torch
 
 from . import (ZERO_BF16, ZERO_FP16, ZERO_STATE_TILE, read_step_state, zero_adamw_step, zero_adamw_step_dev,
+               zero_bucket_segments,
                zero_adamw_step_tiled, zero_adamw_step_tiled_dev, zero_flatten_grads, zero_flatten_grads_sqnorm,
                zero_flatten_plan, zero_grad_sqnorm, zero_grad_sqnorm_workspace_bytes, zero_shard_layout,
                zero_state_tile, zero_state_tiled_numel, zero_state_untile, zero_step_decision, zero_step_decision_dev,
@@ -191,6 +192,70 @@ class DeviceDecision:
 
     def read(self) -> dict:
         """The decided state (synchronizes)."""
+        return read_step_state(self.state)
+
+
+class BucketPipeline:
+    """Constant-capacity buckets for one rank's shard: as backward produces gradients (last tensors first),
+    each bucket of at most `bucket_numel` shard elements is flattened and square-normed on the compute stream
+    as soon as its source tensors are ready, overlapping with the production of the next bucket.  The per-bucket
+    partials land in their own slots; the device decision sums them in bucket order and the update runs over
+    the whole shard.  The bucket capacity is fixed: it does not grow with the model."""
+
+    def __init__(self, shard: "RankShard", sources, bucket_numel: int, cfg: AdamWConfig, loss_scale: float = 1.0,
+                 growth_interval: int = 2**31 - 1):
+        assert shard.fused, "the pipeline flattens and square-norms each bucket in one pass"
+        assert bucket_numel > 0 and bucket_numel % 8 == 0, "whole 16-byte vectors per bucket"
+        self.sh = shard
+        self.cfg = cfg
+        self.sources = sources
+        n = shard.n
+        self.windows = [(a, min(n, a + bucket_numel)) for a in range(0, n, bucket_numel)] or [(0, 0)]
+        k = len(self.windows)
+        dev = shard.device
+        self.norms = torch.zeros(k + (k + 1) // 2, dtype=torch.float64, device=dev)
+        self.sq_base = self.norms.data_ptr()
+        self.flag_base = self.sq_base + 8 * k
+        self.tables, self.counts, self.tensors = [], [], []
+        for a, b in self.windows:
+            segs = zero_bucket_segments(shard.segments, a, b - a)
+            ptrs = [sources[t] if sources[t] is not None else 0 for t in range(len(sources))]
+            blob = zero_flatten_plan(segs, ptrs)
+            table = torch.frombuffer(bytearray(blob), dtype=torch.uint8) if blob else torch.zeros(32, dtype=torch.uint8)
+            self.tables.append(table.to(dev))
+            self.counts.append(len(segs))
+            self.tensors.append(sorted({sg.tensor for sg in segs}))
+        self.state = torch.zeros(16, dtype=torch.float64, device=dev)
+        zero_step_state_init(self.state, loss_scale, growth_interval)
+        self.events = [torch.cuda.Event() for _ in self.windows]
+
+    def step(self, produce=None, producer=None, stream=None) -> None:
+        """One step.  `produce(tensor_indices, stream)` writes those source tensors' gradients (stands in for
+        backward); it runs on `producer` in backward order, one bucket at a time, each followed by an event
+        the compute stream waits for.  Without `produce` the sources are taken as ready."""
+        stream = stream or torch.cuda.current_stream()
+        sh, done = self.sh, set()
+        order = range(len(self.windows) - 1, -1, -1)
+        if produce is not None:
+            producer.wait_stream(stream)  # the previous step has finished reading the sources
+            for k in order:
+                need = [t for t in self.tensors[k] if t not in done]
+                produce(need, producer)
+                done.update(need)
+                self.events[k].record(producer)
+        for k in order:
+            a, b = self.windows[k]
+            if produce is not None:
+                stream.wait_event(self.events[k])
+            zero_flatten_grads_sqnorm(self.tables[k], self.counts[k], sh.grad_dtype, sh.grad.data_ptr() +
+                                      a * sh.grad.element_size(), b - a, sh.ws, sh.ws_bytes, self.sq_base + 8 * k,
+                                      self.flag_base + 4 * k, stream)
+        c = self.cfg
+        zero_step_decision_dev(self.sq_base, self.flag_base, len(self.windows), c.max_norm, self.state, lr=c.lr,
+                               beta1=c.beta1, beta2=c.beta2, eps=c.eps, weight_decay=c.weight_decay, stream=stream)
+        sh.adamw_dev(self.state, stream)
+
+    def read(self) -> dict:
         return read_step_state(self.state)
 
 

@@ -164,3 +164,34 @@ def test_tiled_numel_and_invalid_tiled_args():
     ws = Z.zero_grad_sqnorm_workspace_bytes(100)
     assert lib.zero_flatten_grads_sqnorm(16, 1, 0, 16, 100, 256, ws - 1, 16, 16, None) == Z.ZERO_ERR_INVALID
     assert lib.zero_flatten_grads_sqnorm(12, 1, 0, 16, 100, 256, ws, 16, 16, None) == Z.ZERO_ERR_INVALID
+
+
+def test_bucket_segments_cover_the_shard_once():
+    """Constant-capacity windows over a shard: every valid shard element is covered by exactly one clipped
+    segment, offsets are window-relative, the padding is covered by none, and each clipped piece reads the
+    same tensor element as the unclipped layout."""
+    from synth.workloads import gpt2_tensors
+
+    numels = gpt2_tensors(d=128, layers=2, vocab=500, ctx=32, ffn=512)[1]
+    for world, rank in [(1, 0), (4, 3), (7, 2)]:
+        lay, segs = Z.zero_shard_layout(numels, world, rank)
+        src_of = np.full(lay.shard_numel, -1, np.int64)  # tensor-global element read into each shard slot
+        starts = np.cumsum([0] + numels)
+        for sg in segs:
+            g0 = starts[sg.tensor] + sg.src_offset
+            src_of[sg.dst_offset:sg.dst_offset + sg.numel] = np.arange(g0, g0 + sg.numel)
+        for cap in (8, 1000, 4096, lay.shard_numel + 5):
+            covered = np.zeros(lay.shard_numel, np.int32)
+            for a in range(0, lay.shard_numel, cap):
+                b = min(lay.shard_numel, a + cap)
+                for sg in Z.zero_bucket_segments(segs, a, b - a):
+                    assert sg.numel > 0 and 0 <= sg.dst_offset and sg.dst_offset + sg.numel <= b - a
+                    lo = a + sg.dst_offset
+                    covered[lo:lo + sg.numel] += 1
+                    g0 = starts[sg.tensor] + sg.src_offset
+                    assert (src_of[lo:lo + sg.numel] == np.arange(g0, g0 + sg.numel)).all()
+            assert (covered[:lay.shard_valid] == 1).all() and (covered[lay.shard_valid:] == 0).all()
+    lay, segs = Z.zero_shard_layout([10], 1, 0)
+    assert Z.zero_bucket_segments(segs, 10, 0) == [] and Z.zero_bucket_segments(segs, 3, 0) == []
+    with pytest.raises(Exception):
+        Z.zero_bucket_segments(segs, -1, 4)

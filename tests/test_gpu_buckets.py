@@ -1,0 +1,71 @@
+"""Constant-capacity bucketed pipeline ([Z] section 五（二）, section 四（二）): gradients produced in
+backward order on a producer stream, each bucket flattened and square-normed on the compute stream as soon
+as its tensors are ready, one decision over the bucket partials, one update.  Checked against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth.workloads import gpt2_tensors
+from tests.parity import assert_bf16_within_ulp, assert_bits_equal, assert_f32_close, assert_grad_scale_close
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import mixed_precision_adam_amd as Z
+    from mixed_precision_adam_amd.driver import AdamWConfig, BucketPipeline, RankShard
+
+DEV = "cuda:0"
+SEED = 0x5EED0077
+
+
+SMALL = [5, 17, 3, 40, 11, 1, 64]  # Ψ = 141: ragged everywhere
+
+
+@pytest.mark.parametrize("model,world,rank,bucket", [("gpt2", 2, 0, 65536), ("gpt2", 2, 1, 65536),
+                                                     ("gpt2", 3, 2, 1024), ("gpt2", 1, 0, 1 << 24),
+                                                     ("gpt2", 2, 1, 100_000), ("small", 2, 1, 8),
+                                                     ("small", 3, 0, 16)])
+def test_bucket_pipeline_against_oracle(model, world, rank, bucket):
+    numels = gpt2_tensors(d=128, layers=3, vocab=1000, ctx=64, ffn=512)[1] if model == "gpt2" else SMALL
+    psi = sum(numels)
+    starts = np.cumsum([0] + numels)
+    srcs = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for n in numels]
+    sh = RankShard(numels, world, rank, Z.ZERO_BF16, DEV, sources=srcs, tiled=True, fused=True)
+    lay = sh.layout
+    s = sh.n
+    master = synth.fill_host(synth.field(SEED, synth.STREAM_MASTER, 0, 0.02, synth.F32), lay.shard_offset,
+                             lay.shard_valid)
+    p0 = np.zeros(s, np.float32)
+    p0[:lay.shard_valid] = master
+    sh.load_master(torch.from_numpy(p0).to(DEV))
+    cfg = AdamWConfig(lr=2e-3, beta1=0.9, beta2=0.99, eps=1e-8, weight_decay=0.05, max_norm=0.3)
+    pipe = BucketPipeline(sh, srcs, bucket, cfg)
+    assert len(pipe.windows) == max(1, -(-s // bucket))
+    producer = torch.cuda.Stream()
+    ref = [p0.copy(), np.zeros(s, np.float32), np.zeros(s, np.float32), np.zeros(s, np.uint16)]
+    for t in range(1, 4):
+        field = synth.field(SEED, synth.STREAM_GRAD, t, 1e-3, synth.BF16)
+
+        def produce(idx, stream):
+            for k in idx:
+                synth.fill_device(field, int(starts[k]), numels[k], srcs[k].data_ptr(), stream.cuda_stream)
+
+        pipe.step(produce=produce, producer=producer)
+        got = pipe.read()
+        flat = synth.fill_host(field, 0, psi)
+        g = oracle.flatten([flat], [psi], world, rank)
+        assert_bits_equal(sh.grad.view(torch.int16).cpu().numpy().view(np.uint16), g, f"step {t} shard")
+        sq, fl = oracle.sqnorm(g, oracle.BF16)
+        od = oracle.step_decision([sq], [fl], cfg.max_norm, 1.0, 0, 2**31 - 1)
+        assert got["skip"] == 0 and got["adam_step"] == t
+        same = assert_grad_scale_close(got["grad_scale"], od["grad_scale"], s, f"step {t}")
+        oracle.adamw_step(g, oracle.BF16, *ref, lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps,
+                          weight_decay=cfg.weight_decay, grad_scale=od["grad_scale"], step=t)
+        gp, gm, gv = (x.cpu().numpy() for x in sh.read_state())
+        nd = assert_f32_close(gp, ref[0], "master") + assert_f32_close(gm, ref[1], "m") + \
+            assert_f32_close(gv, ref[2], "v")
+        nd += assert_bf16_within_ulp(sh.param.view(torch.int16).cpu().numpy().view(np.uint16), ref[3], "param")
+        assert nd == 0 or not same, (t, nd)
+
