@@ -100,7 +100,7 @@ def _load():
     lib.orc_cosine_lr.argtypes = [C.c_int64, C.c_int64, C.c_double, C.c_double]
     lib.orc_cosine_lr.restype = C.c_double
     lib.orc_adamw_scalars.argtypes = [C.POINTER(_HParams), C.POINTER(_Scalars)]
-    lib.orc_adamw_step.argtypes = [P, C.c_int32, P, P, P, P, C.c_int64, C.POINTER(_HParams)]
+    lib.orc_adamw_step.argtypes = [P, C.c_int32, P, P, P, P, C.c_int32, C.c_int64, C.POINTER(_HParams)]
     lib.orc_adamw_step_f64.argtypes = [P, P, P, P, C.c_int64, C.POINTER(_HParams)]
     lib.orc_bf16_to_f32.argtypes = [C.c_uint16]
     lib.orc_bf16_to_f32.restype = C.c_float
@@ -109,6 +109,9 @@ def _load():
     lib.orc_f32_to_bf16.argtypes = [C.c_float]
     lib.orc_f32_to_bf16.restype = C.c_uint16
     lib.orc_f32_to_bf16_array.argtypes = [P, P, C.c_int64]
+    lib.orc_f32_to_f16.argtypes = [C.c_float]
+    lib.orc_f32_to_f16.restype = C.c_uint16
+    lib.orc_f32_to_f16_array.argtypes = [P, P, C.c_int64]
     lib.orc_decode_array.argtypes = [P, C.c_int32, P, C.c_int64]
     _lib = lib
     return lib
@@ -258,14 +261,16 @@ def adamw_scalars(lr, beta1, beta2, eps, weight_decay, grad_scale, step) -> dict
 
 
 def adamw_step(grad: np.ndarray, dtype: int, master: np.ndarray, m: np.ndarray, v: np.ndarray, param: np.ndarray, *,
-               lr, beta1, beta2, eps, weight_decay, grad_scale, step) -> None:
-    """In-place update of master / m / v (float32) and param (uint16 bf16 bits)."""
+               lr, beta1, beta2, eps, weight_decay, grad_scale, step, param_dtype: int = BF16) -> None:
+    """In-place update of master / m / v (float32) and param (uint16 bits of bf16, or of fp16 when
+    param_dtype is FP16)."""
     n = grad.size
     assert grad.dtype == np.uint16 and param.dtype == np.uint16
     assert master.dtype == np.float32 and m.dtype == np.float32 and v.dtype == np.float32
     assert master.size == n and m.size == n and v.size == n and param.size == n
     hp = _hp(lr, beta1, beta2, eps, weight_decay, grad_scale, step)
-    rc = _load().orc_adamw_step(_ptr(grad), dtype, _ptr(master), _ptr(m), _ptr(v), _ptr(param), n, C.byref(hp))
+    rc = _load().orc_adamw_step(_ptr(grad), dtype, _ptr(master), _ptr(m), _ptr(v), _ptr(param), param_dtype, n,
+                                C.byref(hp))
     _check(rc, "orc_adamw_step")
 
 
@@ -283,6 +288,13 @@ def f32_to_bf16(x: np.ndarray) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     y = np.empty(x.shape, dtype=np.uint16)
     _load().orc_f32_to_bf16_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def f32_to_f16(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    y = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_f32_to_f16_array(_ptr(x), _ptr(y), x.size)
     return y
 
 

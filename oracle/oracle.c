@@ -58,6 +58,43 @@ uint16_t orc_f32_to_bf16(float f) {
   return (uint16_t)(kept + (uint32_t)round_up);
 }
 
+/* Round a binary32 to the nearest IEEE binary16 value, ties to the value
+ * with an even fraction; a magnitude that rounds past the largest finite
+ * half (65504) becomes infinity.  Done on the exact value in double: for
+ * 2^E <= |x| < 2^(E+1) with E >= -14 the binary16 values are spaced
+ * q = 2^(E-10) apart, and below 2^-14 (subnormals) q = 2^-24; |x|/q is exact
+ * in double and is rounded to an integer k, ties to even; the result is k·q.
+ * A NaN stays a NaN (quiet bit set). */
+uint16_t orc_f32_to_f16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  if (isnan(f)) return (uint16_t)(sign | 0x7E00u | ((u >> 13) & 0x3FFu));
+  if (isinf(f)) return (uint16_t)(sign | 0x7C00u);
+  double a = fabs((double)f);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);  /* 2^(e-1) <= a < 2^e */
+  int E = e - 1;
+  if (E < -14) E = -14;
+  double q = ldexp(1.0, E - 10);
+  double k = a / q;
+  double r = floor(k);
+  double rest = k - r;
+  if (rest > 0.5 || (rest == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  double val = r * q;
+  if (val > 65504.0) return (uint16_t)(sign | 0x7C00u);
+  if (val < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)r); /* zero or subnormal: r·2^-24 */
+  frexp(val, &e);
+  E = e - 1;                                                          /* -14 <= E <= 15 */
+  uint16_t fraction = (uint16_t)(ldexp(val, 10 - E) - 1024.0);        /* val = (1024 + fraction)·2^(E-10) */
+  return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | fraction);
+}
+
+void orc_f32_to_f16_array(const float* x, uint16_t* y, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) y[i] = orc_f32_to_f16(x[i]);
+}
+
 static float orc_decode(uint16_t h, int32_t dtype) {
   return dtype == ORC_BF16 ? orc_bf16_to_f32(h) : orc_f16_to_f32(h);
 }
@@ -313,12 +350,16 @@ int orc_adamw_scalars(const orc_hparams* hp, orc_scalars* s) {
  *   v ← β2·v + (1−β2)·(g·g)
  *   d ← sqrt(v) / sqrt(1−β2^t) + eps
  *   p ← p·(1 − lr·wd) − (lr/(1−β1^t))·(m/d)
- *   param ← bf16_rne(p)                                                    */
+ *   param ← rne16(p)
+ * where rne16 rounds to bf16 or, for fp16 parameters ([Z] section 四（一）:
+ * fp16 parameters and gradients stay whole on every process; [D]: fp16
+ * enabled in the training configuration), to IEEE binary16.                */
 int orc_adamw_step(const uint16_t* grad, int32_t dtype, float* master, float* m, float* v,
-                   uint16_t* param_bf16, int64_t n, const orc_hparams* hp) {
+                   uint16_t* param16, int32_t param_dtype, int64_t n, const orc_hparams* hp) {
   orc_scalars s;
   if (n < 0 || (dtype != ORC_BF16 && dtype != ORC_FP16)) return ORC_ERR_INVALID;
-  if (n > 0 && (!grad || !master || !m || !v || !param_bf16)) return ORC_ERR_INVALID;
+  if (param_dtype != ORC_BF16 && param_dtype != ORC_FP16) return ORC_ERR_INVALID;
+  if (n > 0 && (!grad || !master || !m || !v || !param16)) return ORC_ERR_INVALID;
   if (orc_adamw_scalars(hp, &s) != ORC_OK) return ORC_ERR_INVALID;
   for (int64_t i = 0; i < n; ++i) {
     float g = orc_decode(grad[i], dtype);
@@ -346,7 +387,7 @@ int orc_adamw_step(const uint16_t* grad, int32_t dtype, float* master, float* m,
     m[i] = m_new;
     v[i] = v_new;
     master[i] = p;
-    param_bf16[i] = orc_f32_to_bf16(p);
+    param16[i] = param_dtype == ORC_BF16 ? orc_f32_to_bf16(p) : orc_f32_to_f16(p);
   }
   return ORC_OK;
 }

@@ -85,7 +85,7 @@ double orc_cosine_lr(int64_t t, int64_t total, double lr_max, double lr_min);
 
 int orc_adamw_scalars(const orc_hparams* hp, orc_scalars* out);
 int orc_adamw_step(const uint16_t* grad, int32_t dtype, float* master, float* m, float* v,
-                   uint16_t* param_bf16, int64_t n, const orc_hparams* hp);
+                   uint16_t* param16, int32_t param_dtype, int64_t n, const orc_hparams* hp);
 
 /* Same update in fp64 throughout (no fp32 rounding of state or scalars);
  * used only to bound the fp32 oracle's rounding error. */
@@ -97,6 +97,8 @@ float orc_bf16_to_f32(uint16_t h);
 float orc_f16_to_f32(uint16_t h);
 uint16_t orc_f32_to_bf16(float f);
 void orc_f32_to_bf16_array(const float* x, uint16_t* y, int64_t n);
+uint16_t orc_f32_to_f16(float f);
+void orc_f32_to_f16_array(const float* x, uint16_t* y, int64_t n);
 void orc_decode_array(const uint16_t* x, int32_t dtype, float* y, int64_t n);
 
 #ifdef __cplusplus

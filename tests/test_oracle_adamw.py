@@ -129,6 +129,24 @@ def test_lr_zero_leaves_master_bits():
     assert (m != 0).any() and (v != 0).any()
 
 
+def test_fp16_param_output_is_the_rounded_master():
+    """With fp16 parameters the update is unchanged and the parameter is the master rounded to binary16;
+    the rounding is checked against torch's own conversion (not the oracle's codec)."""
+    hp = dict(lr=1e-2, beta1=0.8, beta2=0.95, eps=1e-3, weight_decay=0.1)
+    master0, grads = _inputs(5000, 3, 8, [0.5] * 3)
+    master0[:4] = [70000.0, -65519.0, 3e-6, 1e-8]  # overflow, round-down, subnormal and underflow parameters
+    p, m, v, qb = _run_oracle(master0, grads, hp, [0.5] * 3)
+    p2, m2, v2 = master0.copy(), np.zeros_like(master0), np.zeros_like(master0)
+    qh = np.zeros(master0.size, np.uint16)
+    for t, g in enumerate(grads, start=1):
+        oracle.adamw_step(g, oracle.BF16, p2, m2, v2, qh, grad_scale=0.5, step=t, param_dtype=oracle.FP16, **hp)
+    for a, b in ((p, p2), (m, m2), (v, v2)):
+        assert (a.view(np.uint32) == b.view(np.uint32)).all()
+    ref = torch.from_numpy(p2.copy()).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert (qh == ref).all() and qh[0] == 0x7C00
+    assert (qb == torch.from_numpy(p.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)).all()
+
+
 def test_zero_betas_sign_like_update():
     hp = dict(lr=1e-3, beta1=0.0, beta2=0.0, eps=1e-8, weight_decay=0.0)
     master0, grads = _inputs(1000, 3, 6, [1.0] * 3)
