@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--unfused", action="store_true", help="flatten and square-norm as two passes")
     ap.add_argument("--decision", choices=("device", "host"), default="device",
                     help="decision on the GPU (no host round trip, default) or on the host after a 16-byte readback")
+    ap.add_argument("--bucket", type=int, default=0,
+                    help="constant bucket capacity in shard elements (0: one pass over the whole shard)")
     ap.add_argument("--event-every", type=int, default=4,
                     help="bracket the kernels of every k-th timed step with HIP events (each record costs ~3 us)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
@@ -138,7 +140,8 @@ def main():
 
     import mixed_precision_adam_amd as Z
     import synth
-    from mixed_precision_adam_amd.driver import AdamWConfig, DeviceDecision, RankShard, ScalerState, wait_spin
+    from mixed_precision_adam_amd.driver import (AdamWConfig, BucketPipeline, DeviceDecision, RankShard,
+                                                 ScalerState, wait_spin)
     from synth.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
@@ -172,6 +175,11 @@ def main():
     scaler = ScalerState(scale=w.loss_scale, growth_interval=growth)
     ddec = DeviceDecision([sh], cfg, loss_scale=w.loss_scale, growth_interval=growth) if args.decision == "device" \
         else None
+    pipe = None
+    if args.bucket:
+        assert ddec is not None and sh.fused, "the bucketed step uses the fused flatten and the device decision"
+        pipe = BucketPipeline(sh, sources, args.bucket, cfg, loss_scale=w.loss_scale, growth_interval=growth)
+        ddec = None
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
@@ -191,6 +199,22 @@ def main():
                                    ctypes.byref(lay_out), ctypes.cast(seg_buf, ctypes.c_void_p), len(segs),
                                    ctypes.byref(nseg))
         assert rc == 0 and nseg.value == len(segs)
+        if pipe is not None:                           # fixed-capacity buckets, last bucket first
+            if e:
+                e[0].record(stream)
+            for k in range(len(pipe.windows) - 1, -1, -1):
+                pipe.reduce_bucket(k, stream)          # a2 + a3 of one bucket
+            if e:
+                e[1].record(stream)
+            pipe.decide(stream)                        # a4 over the bucket partials
+            if e:
+                e[4].record(stream)
+            sh.adamw_dev(pipe.state, stream)           # a5
+            if e:
+                e[5].record(stream)
+                ev["flatten"].append((e[0], e[1]))
+                ev["adamw"].append((e[4], e[5]))
+            return None
         if ddec is not None:                           # everything on the GPU, nothing waits on the host
             if e:
                 e[0].record(stream)
@@ -252,8 +276,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    if ddec is not None:
-        st = ddec.read()
+    if ddec is not None or pipe is not None:
+        st = (ddec or pipe).read()
         dec = {"global_norm": st["global_norm"], "grad_scale": st["grad_scale"], "skip": st["skip"]}
 
     def avg_ms(pairs):
@@ -298,6 +322,8 @@ def main():
             "adamw_params_per_s": S / (ms["adamw"] * 1e-3),
             "state_layout": args.state,
             "decision": args.decision,
+            "bucket_numel": args.bucket or None,
+            "buckets": len(pipe.windows) if pipe is not None else None,
             "flatten_norm_fused": sh.fused,
             "flatten_ms": ms["flatten"],
             "flatten_gbs": FLATTEN_BYTES_PER_PARAM * S / (ms["flatten"] * 1e-3) / 1e9,

@@ -220,7 +220,11 @@ double zero_cosine_lr(int64_t t, int64_t total, double lr_max, double lr_min);
  *   v = (b2·v) + (omb2·(g·g))
  *   d = ((sqrt(v) / bc2_sqrt) + eps)
  *   p = (p·decay) − (step_size·(m/d))
- *   param = bf16 round-to-nearest-even of p (NaN stays NaN)
+ *   param = p rounded to the parameter format pdt, nearest, ties to even:
+ *           bf16, or IEEE binary16 for fp16 parameters ([Z] section 四（一）
+ *           keeps fp16 parameters and gradients whole on every process; [D]
+ *           trains with fp16 enabled); binary16 overflows to infinity and
+ *           keeps subnormals.  NaN stays NaN.
  */
 typedef struct zero_adamw_hparams {
   double lr;           /* >= 0 */
@@ -232,13 +236,14 @@ typedef struct zero_adamw_hparams {
 } zero_adamw_hparams;
 
 /* Device.  grad_dev: n gradients (bf16 or fp16, per gdt); master/m/v: n fp32
- * each, updated in place; param_dev: n bf16 written (never read).  Buffers
+ * each, updated in place; param_dev: n 16-bit parameters in format pdt
+ * (ZERO_BF16 or ZERO_FP16), written (never read).  Buffers
  * must be aligned to their element size.  When grad and param are 8-byte
  * aligned and master/m/v 16-byte aligned the kernel streams whole vectors;
  * otherwise (and for the last n mod 4 elements) it updates element by
  * element with identical results. */
 int zero_adamw_step(const void* grad_dev, zero_dtype gdt, float* master_dev, float* m_dev, float* v_dev,
-                    uint16_t* param_dev, int64_t n, const zero_adamw_hparams* hp, void* stream);
+                    uint16_t* param_dev, zero_dtype pdt, int64_t n, const zero_adamw_hparams* hp, void* stream);
 
 /* Tiled optimizer state: the same fp32 master / m / v, interleaved in tiles of
  * ZERO_STATE_TILE elements.  Tile k holds master[T·k .. T·k+T), then m[...],
@@ -250,8 +255,8 @@ int zero_adamw_step(const void* grad_dev, zero_dtype gdt, float* master_dev, flo
  * per-element operations, same bits); state_dev must be 16-byte aligned. */
 #define ZERO_STATE_TILE 1024
 int64_t zero_state_tiled_numel(int64_t n);
-int zero_adamw_step_tiled(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev, int64_t n,
-                          const zero_adamw_hparams* hp, void* stream);
+int zero_adamw_step_tiled(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev,
+                          zero_dtype pdt, int64_t n, const zero_adamw_hparams* hp, void* stream);
 /* Device bit copies between separate master/m/v arrays and the tiled state
  * (for initialisation and checkpoints); padding floats are left untouched. */
 int zero_state_tile(const float* master_dev, const float* m_dev, const float* v_dev, float* state_dev, int64_t n,
@@ -299,9 +304,10 @@ int zero_step_decision_dev(const double* rank_sqnorms_dev, const int32_t* rank_f
  * from the device state; when state_dev->skip is set the kernels return
  * without touching memory. */
 int zero_adamw_step_dev(const void* grad_dev, zero_dtype gdt, float* master_dev, float* m_dev, float* v_dev,
-                        uint16_t* param_dev, int64_t n, const zero_step_state* state_dev, void* stream);
-int zero_adamw_step_tiled_dev(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev, int64_t n,
-                              const zero_step_state* step_state_dev, void* stream);
+                        uint16_t* param_dev, zero_dtype pdt, int64_t n, const zero_step_state* state_dev,
+                        void* stream);
+int zero_adamw_step_tiled_dev(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev,
+                              zero_dtype pdt, int64_t n, const zero_step_state* step_state_dev, void* stream);
 
 #ifdef __cplusplus
 }

@@ -86,18 +86,19 @@ _lib.zero_clip_coef.restype = C.c_double
 _lib.zero_loss_scale_update.argtypes = [C.POINTER(C.c_double), C.c_int32, C.POINTER(C.c_int32), C.c_int32]
 _lib.zero_cosine_lr.argtypes = [C.c_int64, C.c_int64, C.c_double, C.c_double]
 _lib.zero_cosine_lr.restype = C.c_double
-_lib.zero_adamw_step.argtypes = [_P, C.c_int, _P, _P, _P, _P, C.c_int64, C.POINTER(zero_adamw_hparams), _P]
+_lib.zero_adamw_step.argtypes = [_P, C.c_int, _P, _P, _P, _P, C.c_int, C.c_int64, C.POINTER(zero_adamw_hparams),
+                                 _P]
 _lib.zero_flatten_grads_sqnorm.argtypes = [_P, C.c_int32, C.c_int, _P, C.c_int64, _P, C.c_size_t, _P, _P, _P]
 _lib.zero_state_tiled_numel.argtypes = [C.c_int64]
 _lib.zero_state_tiled_numel.restype = C.c_int64
-_lib.zero_adamw_step_tiled.argtypes = [_P, C.c_int, _P, _P, C.c_int64, C.POINTER(zero_adamw_hparams), _P]
+_lib.zero_adamw_step_tiled.argtypes = [_P, C.c_int, _P, _P, C.c_int, C.c_int64, C.POINTER(zero_adamw_hparams), _P]
 _lib.zero_state_tile.argtypes = [_P, _P, _P, _P, C.c_int64, _P]
 _lib.zero_state_untile.argtypes = [_P, _P, _P, _P, C.c_int64, _P]
 
 _lib.zero_step_state_init.argtypes = [_P, C.c_double, C.c_int32, _P]
 _lib.zero_step_decision_dev.argtypes = [_P, _P, C.c_int32, C.c_double, C.POINTER(zero_adamw_hparams), _P, _P]
-_lib.zero_adamw_step_dev.argtypes = [_P, C.c_int, _P, _P, _P, _P, C.c_int64, _P, _P]
-_lib.zero_adamw_step_tiled_dev.argtypes = [_P, C.c_int, _P, _P, C.c_int64, _P, _P]
+_lib.zero_adamw_step_dev.argtypes = [_P, C.c_int, _P, _P, _P, _P, C.c_int, C.c_int64, _P, _P]
+_lib.zero_adamw_step_tiled_dev.argtypes = [_P, C.c_int, _P, _P, C.c_int, C.c_int64, _P, _P]
 
 ZERO_STATE_TILE = 1024  # include/zero_shard.h
 
@@ -245,9 +246,10 @@ def zero_cosine_lr(t: int, total: int, lr_max: float, lr_min: float) -> float:
 
 
 def zero_adamw_step(grad, dtype: int, master, m, v, param, n: int, *, lr: float, beta1: float, beta2: float,
-                    eps: float, weight_decay: float, grad_scale: float, step: int, stream=None) -> None:
+                    eps: float, weight_decay: float, grad_scale: float, step: int, stream=None,
+                    param_dtype: int = ZERO_BF16) -> None:
     hp = zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, grad_scale, step)
-    _check(_lib.zero_adamw_step(_addr(grad), dtype, _addr(master), _addr(m), _addr(v), _addr(param), n,
+    _check(_lib.zero_adamw_step(_addr(grad), dtype, _addr(master), _addr(m), _addr(v), _addr(param), param_dtype, n,
                                 C.byref(hp), _stream(stream)))
 
 
@@ -262,9 +264,10 @@ def zero_state_tiled_numel(n: int) -> int:
 
 
 def zero_adamw_step_tiled(grad, dtype: int, state, param, n: int, *, lr: float, beta1: float, beta2: float,
-                          eps: float, weight_decay: float, grad_scale: float, step: int, stream=None) -> None:
+                          eps: float, weight_decay: float, grad_scale: float, step: int, stream=None,
+                          param_dtype: int = ZERO_BF16) -> None:
     hp = zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, grad_scale, step)
-    _check(_lib.zero_adamw_step_tiled(_addr(grad), dtype, _addr(state), _addr(param), n, C.byref(hp),
+    _check(_lib.zero_adamw_step_tiled(_addr(grad), dtype, _addr(state), _addr(param), param_dtype, n, C.byref(hp),
                                       _stream(stream)))
 
 
@@ -287,14 +290,16 @@ def zero_step_decision_dev(rank_sqnorms, rank_flags, n_ranks: int, max_norm: flo
                                        _addr(state), _stream(stream)))
 
 
-def zero_adamw_step_dev(grad, dtype: int, master, m, v, param, n: int, step_state, stream=None) -> None:
-    _check(_lib.zero_adamw_step_dev(_addr(grad), dtype, _addr(master), _addr(m), _addr(v), _addr(param), n,
-                                    _addr(step_state), _stream(stream)))
+def zero_adamw_step_dev(grad, dtype: int, master, m, v, param, n: int, step_state, stream=None,
+                        param_dtype: int = ZERO_BF16) -> None:
+    _check(_lib.zero_adamw_step_dev(_addr(grad), dtype, _addr(master), _addr(m), _addr(v), _addr(param), param_dtype,
+                                    n, _addr(step_state), _stream(stream)))
 
 
-def zero_adamw_step_tiled_dev(grad, dtype: int, state, param, n: int, step_state, stream=None) -> None:
-    _check(_lib.zero_adamw_step_tiled_dev(_addr(grad), dtype, _addr(state), _addr(param), n, _addr(step_state),
-                                          _stream(stream)))
+def zero_adamw_step_tiled_dev(grad, dtype: int, state, param, n: int, step_state, stream=None,
+                              param_dtype: int = ZERO_BF16) -> None:
+    _check(_lib.zero_adamw_step_tiled_dev(_addr(grad), dtype, _addr(state), _addr(param), param_dtype, n,
+                                          _addr(step_state), _stream(stream)))
 
 
 def read_step_state(state_tensor) -> dict:

@@ -74,6 +74,19 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// fp32 -> the parameter format PT (bf16 or IEEE binary16), round to nearest,
+// ties to even.  The binary16 conversion is the hardware's (v_cvt_f16_f32 in
+// the default round-to-nearest-even mode, binary16 denormals kept): overflow
+// gives infinity, tiny values become subnormals or zero.
+template <int PT>
+__device__ __forceinline__ uint32_t narrow(float f) {
+  if constexpr (PT == ZERO_BF16) {
+    return bf16_rne(f);
+  } else {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+  }
+}
+
 // ------------------------------------------------------------------ AdamW
 
 struct AdamScalars {
@@ -130,8 +143,8 @@ __device__ __forceinline__ void st_stream(T* p, T v) {
 }
 
 // Four consecutive elements: grads as two 32-bit words (2 x 16-bit each), the
-// fp32 state as one 16-byte vector per array.  Returns the four bf16 params.
-template <int DT>
+// fp32 state as one 16-byte vector per array.  Returns the four 16-bit params.
+template <int DT, int PT>
 __device__ __forceinline__ u32x2 adam_unit4(u32x2 g, f32x4& p, f32x4& m, f32x4& v, const AdamScalars& s) {
   u32x2 out;
 #pragma unroll
@@ -146,14 +159,14 @@ __device__ __forceinline__ u32x2 adam_unit4(u32x2 g, f32x4& p, f32x4& m, f32x4& 
     m[c + 1] = m1;
     v[c] = v0;
     v[c + 1] = v1;
-    out[w] = bf16_rne(p0) | (bf16_rne(p1) << 16);
+    out[w] = narrow<PT>(p0) | (narrow<PT>(p1) << 16);
   }
   return out;
 }
 
 // The last, partial group of four elements (at most one per launch): element
 // by element, touching nothing at or past n.
-template <int DT>
+template <int DT, int PT>
 __device__ __forceinline__ void adam_partial4(const uint16_t* __restrict__ grad, float* __restrict__ p,
                                               float* __restrict__ m, float* __restrict__ v,
                                               uint16_t* __restrict__ param, int64_t e, int64_t n,
@@ -164,7 +177,7 @@ __device__ __forceinline__ void adam_partial4(const uint16_t* __restrict__ grad,
     p[i - e] = pi;
     m[i - e] = mi;
     v[i - e] = vi;
-    param[i] = static_cast<uint16_t>(bf16_rne(pi));
+    param[i] = static_cast<uint16_t>(narrow<PT>(pi));
   }
 }
 
@@ -174,7 +187,7 @@ __device__ __forceinline__ void adam_partial4(const uint16_t* __restrict__ grad,
 // arrays, 512 B for grads and params).  All loads of the workgroup's U units
 // are issued before the arithmetic.  The thread whose group straddles n
 // finishes the ragged tail element by element.
-template <int DT, int U>
+template <int DT, int PT, int U>
 __global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const uint16_t* __restrict__ grad16,
                                                            float* __restrict__ master, float* __restrict__ mom,
                                                            float* __restrict__ var, uint16_t* __restrict__ param16,
@@ -203,14 +216,14 @@ __global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const uint16_t* __res
   for (int u = 0; u < U; ++u) {
     const int64_t i = first + static_cast<int64_t>(u) * kBlock;
     if (i < n4) {
-      const u32x2 q = adam_unit4<DT>(g[u], p[u], m[u], v[u], s);
+      const u32x2 q = adam_unit4<DT, PT>(g[u], p[u], m[u], v[u], s);
       st_stream(p4 + i, p[u]);
       st_stream(m4 + i, m[u]);
       st_stream(v4 + i, v[u]);
       st_stream(param + i, q);
     } else if (i == n4 && 4 * n4 < n) {
       const int64_t e = 4 * n4;
-      adam_partial4<DT>(grad16, master + e, mom + e, var + e, param16, e, n, s);
+      adam_partial4<DT, PT>(grad16, master + e, mom + e, var + e, param16, e, n, s);
     }
   }
 }
@@ -232,7 +245,7 @@ constexpr int kTileUnits = 1;
 constexpr int64_t kTile4 = kTile / 4;  // 16-byte vectors per array per tile
 static_assert(kTile4 == kBlock * kTileUnits, "each thread owns kTileUnits groups of 4 elements of a tile");
 
-template <int DT>
+template <int DT, int PT>
 __global__ __launch_bounds__(kBlock) void adamw_tiled_kernel(const uint16_t* __restrict__ grad16,
                                                              f32x4* __restrict__ state,
                                                              uint16_t* __restrict__ param16, int64_t n,
@@ -260,21 +273,21 @@ __global__ __launch_bounds__(kBlock) void adamw_tiled_kernel(const uint16_t* __r
     const int j = threadIdx.x + u * kBlock;
     const int64_t e = tile * kTile + 4 * static_cast<int64_t>(j);
     if (e + 4 <= n) {
-      const u32x2 q = adam_unit4<DT>(g[u], p[u], m[u], v[u], s);
+      const u32x2 q = adam_unit4<DT, PT>(g[u], p[u], m[u], v[u], s);
       st_stream(base + j, p[u]);
       st_stream(base + kTile4 + j, m[u]);
       st_stream(base + 2 * kTile4 + j, v[u]);
       st_stream(reinterpret_cast<u32x2*>(param16 + e), q);
     } else if (e < n) {
       float* f = reinterpret_cast<float*>(base + j);
-      adam_partial4<DT>(grad16, f, f + kTile, f + 2 * kTile, param16, e, n, s);
+      adam_partial4<DT, PT>(grad16, f, f + kTile, f + 2 * kTile, param16, e, n, s);
     }
   }
 }
 
 // Element paths for ragged tails and unaligned buffers: the same update, one
 // element per thread, grid-stride.  TILED selects the state addressing.
-template <int DT, bool TILED>
+template <int DT, int PT, bool TILED>
 __global__ __launch_bounds__(kBlock) void adamw_element_kernel(const uint16_t* __restrict__ grad,
                                                                float* __restrict__ master, float* __restrict__ mom,
                                                                float* __restrict__ var, uint16_t* __restrict__ param,
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(kBlock) void adamw_element_kernel(const uint16_t* _
     master[ip] = p;
     mom[im] = m;
     var[iv] = v;
-    param[i] = static_cast<uint16_t>(bf16_rne(p));
+    param[i] = static_cast<uint16_t>(narrow<PT>(p));
   }
 }
 
@@ -557,9 +570,10 @@ bool dtype_ok(int dt) { return dt == ZERO_BF16 || dt == ZERO_FP16; }
 
 // Validates the arguments shared by both AdamW entry points and derives the
 // fp32 scalars from fp64 host arithmetic (each rounded once).
-int adam_args_ok(const char* fn, const void* grad_dev, int gdt, const void* param_dev, int64_t n,
+int adam_args_ok(const char* fn, const void* grad_dev, int gdt, const void* param_dev, int pdt, int64_t n,
                  const zero_adamw_hparams* hp, AdamScalars* s) {
   if (!dtype_ok(gdt)) return fail(ZERO_ERR_INVALID, "%s: unknown dtype %d", fn, gdt);
+  if (!dtype_ok(pdt)) return fail(ZERO_ERR_INVALID, "%s: unknown parameter dtype %d", fn, pdt);
   if (!hp) return fail(ZERO_ERR_INVALID, "%s: hparams NULL", fn);
   if (n < 0) return fail(ZERO_ERR_INVALID, "%s: n < 0", fn);
   if (n > 0 && (!grad_dev || !param_dev)) return fail(ZERO_ERR_INVALID, "%s: NULL grad or param", fn);
@@ -584,23 +598,37 @@ int adam_args_ok(const char* fn, const void* grad_dev, int gdt, const void* para
   return ZERO_OK;
 }
 
+// Calls f(Formats<G, P>{}) for the run-time (gradient, parameter) format pair,
+// so each launcher names its kernel template once.
+template <int G, int P>
+struct Formats {
+  static constexpr int grad = G, param = P;
+};
+template <typename F>
+void with_formats(int gdt, int pdt, F&& f) {
+  if (gdt == ZERO_BF16) {
+    if (pdt == ZERO_BF16) f(Formats<ZERO_BF16, ZERO_BF16>{}); else f(Formats<ZERO_BF16, ZERO_FP16>{});
+  } else {
+    if (pdt == ZERO_BF16) f(Formats<ZERO_FP16, ZERO_BF16>{}); else f(Formats<ZERO_FP16, ZERO_FP16>{});
+  }
+}
+
 template <bool TILED>
-int launch_elements(const uint16_t* grad, int gdt, float* master, float* m, float* v, uint16_t* param, int64_t begin,
-                    int64_t n, const AdamScalars& s, const zero_step_state* dev, hipStream_t st, const char* what) {
+int launch_elements(const uint16_t* grad, int gdt, float* master, float* m, float* v, uint16_t* param, int pdt,
+                    int64_t begin, int64_t n, const AdamScalars& s, const zero_step_state* dev, hipStream_t st,
+                    const char* what) {
   if (begin >= n) return ZERO_OK;
   const int64_t blocks = std::min<int64_t>((n - begin + kBlock - 1) / kBlock, 65536);
-  if (gdt == ZERO_BF16) {
-    hipLaunchKernelGGL((adamw_element_kernel<ZERO_BF16, TILED>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                       st, grad, master, m, v, param, begin, n, s, dev);
-  } else {
-    hipLaunchKernelGGL((adamw_element_kernel<ZERO_FP16, TILED>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                       st, grad, master, m, v, param, begin, n, s, dev);
-  }
+  with_formats(gdt, pdt, [&](auto fm) {
+    using FM = decltype(fm);
+    hipLaunchKernelGGL((adamw_element_kernel<FM::grad, FM::param, TILED>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kBlock), 0, st, grad, master, m, v, param, begin, n, s, dev);
+  });
   return launch_status(what);
 }
 
 int launch_adamw_arrays(const char* fn, const void* grad_dev, int gdt, float* master_dev, float* m_dev, float* v_dev,
-                        uint16_t* param_dev, int64_t n, const AdamScalars& s, const zero_step_state* dev,
+                        uint16_t* param_dev, int pdt, int64_t n, const AdamScalars& s, const zero_step_state* dev,
                         hipStream_t st) {
   if (n > 0 && (!master_dev || !m_dev || !v_dev)) return fail(ZERO_ERR_INVALID, "%s: NULL state", fn);
   if (((reinterpret_cast<uintptr_t>(master_dev) | reinterpret_cast<uintptr_t>(m_dev) |
@@ -610,43 +638,40 @@ int launch_adamw_arrays(const char* fn, const void* grad_dev, int gdt, float* ma
   const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
   const bool vec = aligned8(grad_dev) && aligned8(param_dev) && aligned16(master_dev) && aligned16(m_dev) &&
                    aligned16(v_dev);
-  if (!vec) return launch_elements<false>(g, gdt, master_dev, m_dev, v_dev, param_dev, 0, n, s, dev, st, fn);
+  if (!vec) return launch_elements<false>(g, gdt, master_dev, m_dev, v_dev, param_dev, pdt, 0, n, s, dev, st, fn);
   constexpr int64_t per = kBlock * kAdamUnroll;
   const int64_t groups = (n + 3) / 4;  // the last one may be partial
   const int64_t blocks = (groups + per - 1) / per;
-  if (gdt == ZERO_BF16) {
-    hipLaunchKernelGGL((adamw_vec_kernel<ZERO_BF16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                       st, g, master_dev, m_dev, v_dev, param_dev, n, s, dev);
-  } else {
-    hipLaunchKernelGGL((adamw_vec_kernel<ZERO_FP16, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
-                       st, g, master_dev, m_dev, v_dev, param_dev, n, s, dev);
-  }
+  with_formats(gdt, pdt, [&](auto fm) {
+    using FM = decltype(fm);
+    hipLaunchKernelGGL((adamw_vec_kernel<FM::grad, FM::param, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kBlock), 0, st, g, master_dev, m_dev, v_dev, param_dev, n, s, dev);
+  });
   return launch_status(fn);
 }
 
-int launch_adamw_tiled(const char* fn, const void* grad_dev, int gdt, float* state_dev, uint16_t* param_dev, int64_t n,
-                       const AdamScalars& s, const zero_step_state* dev, hipStream_t st) {
+int launch_adamw_tiled(const char* fn, const void* grad_dev, int gdt, float* state_dev, uint16_t* param_dev, int pdt,
+                       int64_t n, const AdamScalars& s, const zero_step_state* dev, hipStream_t st) {
   if (n > 0 && !state_dev) return fail(ZERO_ERR_INVALID, "%s: NULL state", fn);
   if (!aligned16(state_dev)) return fail(ZERO_ERR_INVALID, "%s: state must be 16-byte aligned", fn);
   if (n == 0) return ZERO_OK;
   const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
   if (!aligned8(grad_dev) || !aligned8(param_dev))
-    return launch_elements<true>(g, gdt, state_dev, state_dev, state_dev, param_dev, 0, n, s, dev, st, fn);
+    return launch_elements<true>(g, gdt, state_dev, state_dev, state_dev, param_dev, pdt, 0, n, s, dev, st, fn);
   const int64_t tiles = (n + kTile - 1) / kTile;
   auto* state = reinterpret_cast<f32x4*>(state_dev);
-  if (gdt == ZERO_BF16) {
-    hipLaunchKernelGGL(adamw_tiled_kernel<ZERO_BF16>, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, st, g,
-                       state, param_dev, n, s, dev);
-  } else {
-    hipLaunchKernelGGL(adamw_tiled_kernel<ZERO_FP16>, dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0, st, g,
-                       state, param_dev, n, s, dev);
-  }
+  with_formats(gdt, pdt, [&](auto fm) {
+    using FM = decltype(fm);
+    hipLaunchKernelGGL((adamw_tiled_kernel<FM::grad, FM::param>), dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0,
+                       st, g, state, param_dev, n, s, dev);
+  });
   return launch_status(fn);
 }
 
-int dev_args_ok(const char* fn, const void* grad_dev, int gdt, const void* param_dev, int64_t n,
+int dev_args_ok(const char* fn, const void* grad_dev, int gdt, const void* param_dev, int pdt, int64_t n,
                 const zero_step_state* dev) {
   if (!dtype_ok(gdt)) return fail(ZERO_ERR_INVALID, "%s: unknown dtype %d", fn, gdt);
+  if (!dtype_ok(pdt)) return fail(ZERO_ERR_INVALID, "%s: unknown parameter dtype %d", fn, pdt);
   if (!dev || !aligned16(dev)) return fail(ZERO_ERR_INVALID, "%s: step state NULL or not 16-byte aligned", fn);
   if (n < 0) return fail(ZERO_ERR_INVALID, "%s: n < 0", fn);
   if (n > 0 && (!grad_dev || !param_dev)) return fail(ZERO_ERR_INVALID, "%s: NULL grad or param", fn);
@@ -981,19 +1006,20 @@ double zero_cosine_lr(int64_t t, int64_t total, double lr_max, double lr_min) {
 }
 
 int zero_adamw_step(const void* grad_dev, zero_dtype gdt, float* master_dev, float* m_dev, float* v_dev,
-                    uint16_t* param_dev, int64_t n, const zero_adamw_hparams* hp, void* stream) {
+                    uint16_t* param_dev, zero_dtype pdt, int64_t n, const zero_adamw_hparams* hp, void* stream) {
   AdamScalars s;
-  int rc = adam_args_ok("zero_adamw_step", grad_dev, gdt, param_dev, n, hp, &s);
+  int rc = adam_args_ok("zero_adamw_step", grad_dev, gdt, param_dev, pdt, n, hp, &s);
   if (rc != ZERO_OK) return rc;
-  return launch_adamw_arrays("zero_adamw_step", grad_dev, gdt, master_dev, m_dev, v_dev, param_dev, n, s, nullptr,
-                             static_cast<hipStream_t>(stream));
+  return launch_adamw_arrays("zero_adamw_step", grad_dev, gdt, master_dev, m_dev, v_dev, param_dev, pdt, n, s,
+                             nullptr, static_cast<hipStream_t>(stream));
 }
 
 int zero_adamw_step_dev(const void* grad_dev, zero_dtype gdt, float* master_dev, float* m_dev, float* v_dev,
-                        uint16_t* param_dev, int64_t n, const zero_step_state* state_dev, void* stream) {
-  int rc = dev_args_ok("zero_adamw_step_dev", grad_dev, gdt, param_dev, n, state_dev);
+                        uint16_t* param_dev, zero_dtype pdt, int64_t n, const zero_step_state* state_dev,
+                        void* stream) {
+  int rc = dev_args_ok("zero_adamw_step_dev", grad_dev, gdt, param_dev, pdt, n, state_dev);
   if (rc != ZERO_OK) return rc;
-  return launch_adamw_arrays("zero_adamw_step_dev", grad_dev, gdt, master_dev, m_dev, v_dev, param_dev, n,
+  return launch_adamw_arrays("zero_adamw_step_dev", grad_dev, gdt, master_dev, m_dev, v_dev, param_dev, pdt, n,
                              AdamScalars{}, state_dev, static_cast<hipStream_t>(stream));
 }
 
@@ -1002,20 +1028,20 @@ int64_t zero_state_tiled_numel(int64_t n) {
   return 3 * kTile * ((n + kTile - 1) / kTile);
 }
 
-int zero_adamw_step_tiled(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev, int64_t n,
-                          const zero_adamw_hparams* hp, void* stream) {
+int zero_adamw_step_tiled(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev,
+                          zero_dtype pdt, int64_t n, const zero_adamw_hparams* hp, void* stream) {
   AdamScalars s;
-  int rc = adam_args_ok("zero_adamw_step_tiled", grad_dev, gdt, param_dev, n, hp, &s);
+  int rc = adam_args_ok("zero_adamw_step_tiled", grad_dev, gdt, param_dev, pdt, n, hp, &s);
   if (rc != ZERO_OK) return rc;
-  return launch_adamw_tiled("zero_adamw_step_tiled", grad_dev, gdt, state_dev, param_dev, n, s, nullptr,
+  return launch_adamw_tiled("zero_adamw_step_tiled", grad_dev, gdt, state_dev, param_dev, pdt, n, s, nullptr,
                             static_cast<hipStream_t>(stream));
 }
 
-int zero_adamw_step_tiled_dev(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev, int64_t n,
-                              const zero_step_state* step_state_dev, void* stream) {
-  int rc = dev_args_ok("zero_adamw_step_tiled_dev", grad_dev, gdt, param_dev, n, step_state_dev);
+int zero_adamw_step_tiled_dev(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev,
+                              zero_dtype pdt, int64_t n, const zero_step_state* step_state_dev, void* stream) {
+  int rc = dev_args_ok("zero_adamw_step_tiled_dev", grad_dev, gdt, param_dev, pdt, n, step_state_dev);
   if (rc != ZERO_OK) return rc;
-  return launch_adamw_tiled("zero_adamw_step_tiled_dev", grad_dev, gdt, state_dev, param_dev, n, AdamScalars{},
+  return launch_adamw_tiled("zero_adamw_step_tiled_dev", grad_dev, gdt, state_dev, param_dev, pdt, n, AdamScalars{},
                             step_state_dev, static_cast<hipStream_t>(stream));
 }
 

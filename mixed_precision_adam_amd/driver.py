@@ -44,10 +44,11 @@ class ScalerState:
 
 class RankShard:
     """One simulated rank: the flat 16-bit grad shard, the fp32 master/m/v state (three arrays, or one
-    tiled array when ``tiled``), the bf16 param shard and the norm scratch."""
+    tiled array when ``tiled``), the 16-bit param shard (bf16, or fp16 with ``param_dtype=ZERO_FP16``) and
+    the norm scratch."""
 
     def __init__(self, numels, world: int, rank: int, grad_dtype: int, device="cuda", sources=None,
-                 tiled: bool = False, fused: bool = False):
+                 tiled: bool = False, fused: bool = False, param_dtype: int = ZERO_BF16):
         self.layout, self.segments = zero_shard_layout(numels, world, rank)
         self.grad_dtype = grad_dtype
         self.device = torch.device(device)
@@ -62,7 +63,8 @@ class RankShard:
             self.master = torch.zeros(n, dtype=torch.float32, device=self.device)
             self.m = torch.zeros(n, dtype=torch.float32, device=self.device)
             self.v = torch.zeros(n, dtype=torch.float32, device=self.device)
-        self.param = torch.zeros(n, dtype=torch.bfloat16, device=self.device)
+        self.param_dtype = param_dtype
+        self.param = torch.zeros(n, dtype=_TORCH16[param_dtype], device=self.device)
         self.ws_bytes = zero_grad_sqnorm_workspace_bytes(n)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         # square-norm (double) and non-finite flag (int32) side by side: one 16-byte readback per step
@@ -143,14 +145,15 @@ class RankShard:
     def adamw_dev(self, step_state, stream=None) -> None:
         """The update with its scalars taken from a device-resident zero_step_state."""
         if self.tiled:
-            zero_adamw_step_tiled_dev(self.grad, self.grad_dtype, self.state, self.param, self.n, step_state, stream)
+            zero_adamw_step_tiled_dev(self.grad, self.grad_dtype, self.state, self.param, self.n, step_state, stream,
+                                      param_dtype=self.param_dtype)
         else:
             zero_adamw_step_dev(self.grad, self.grad_dtype, self.master, self.m, self.v, self.param, self.n,
-                                step_state, stream)
+                                step_state, stream, param_dtype=self.param_dtype)
 
     def adamw(self, cfg: AdamWConfig, grad_scale: float, step: int, stream=None) -> None:
         kw = dict(lr=cfg.lr, beta1=cfg.beta1, beta2=cfg.beta2, eps=cfg.eps, weight_decay=cfg.weight_decay,
-                  grad_scale=grad_scale, step=step, stream=stream)
+                  grad_scale=grad_scale, step=step, stream=stream, param_dtype=self.param_dtype)
         if self.tiled:
             zero_adamw_step_tiled(self.grad, self.grad_dtype, self.state, self.param, self.n, **kw)
         else:
@@ -234,7 +237,7 @@ class BucketPipeline:
         backward); it runs on `producer` in backward order, one bucket at a time, each followed by an event
         the compute stream waits for.  Without `produce` the sources are taken as ready."""
         stream = stream or torch.cuda.current_stream()
-        sh, done = self.sh, set()
+        done = set()
         order = range(len(self.windows) - 1, -1, -1)
         if produce is not None:
             producer.wait_stream(stream)  # the previous step has finished reading the sources
@@ -244,16 +247,25 @@ class BucketPipeline:
                 done.update(need)
                 self.events[k].record(producer)
         for k in order:
-            a, b = self.windows[k]
             if produce is not None:
                 stream.wait_event(self.events[k])
-            zero_flatten_grads_sqnorm(self.tables[k], self.counts[k], sh.grad_dtype, sh.grad.data_ptr() +
-                                      a * sh.grad.element_size(), b - a, sh.ws, sh.ws_bytes, self.sq_base + 8 * k,
-                                      self.flag_base + 4 * k, stream)
+            self.reduce_bucket(k, stream)
+        self.decide(stream)
+        self.sh.adamw_dev(self.state, stream)
+
+    def reduce_bucket(self, k: int, stream=None) -> None:
+        """Flatten + square-norm partial of bucket k into its own slot."""
+        sh = self.sh
+        a, b = self.windows[k]
+        zero_flatten_grads_sqnorm(self.tables[k], self.counts[k], sh.grad_dtype, sh.grad.data_ptr() +
+                                  a * sh.grad.element_size(), b - a, sh.ws, sh.ws_bytes, self.sq_base + 8 * k,
+                                  self.flag_base + 4 * k, stream)
+
+    def decide(self, stream=None) -> None:
+        """The device decision over the per-bucket partials (summed in bucket order)."""
         c = self.cfg
         zero_step_decision_dev(self.sq_base, self.flag_base, len(self.windows), c.max_norm, self.state, lr=c.lr,
                                beta1=c.beta1, beta2=c.beta2, eps=c.eps, weight_decay=c.weight_decay, stream=stream)
-        sh.adamw_dev(self.state, stream)
 
     def read(self) -> dict:
         return read_step_state(self.state)

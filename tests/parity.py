@@ -41,7 +41,8 @@ def assert_f32_close(got: np.ndarray, ref: np.ndarray, what: str, rel: float = R
 
 
 def assert_bf16_within_ulp(got: np.ndarray, ref: np.ndarray, what: str, ulps: int = 1) -> int:
-    """bf16 bit patterns (uint16). Compares positions on the ordered number line."""
+    """16-bit float bit patterns (uint16; bf16 or fp16, both sign-magnitude). Compares positions on the
+    ordered number line."""
     def ordered(x):
         x = x.astype(np.int32)
         return np.where(x & 0x8000, -(x & 0x7FFF), x)
@@ -74,3 +75,21 @@ def assert_grad_scale_close(got: float, ref: float, n: int, what: str) -> bool:
     bound = max(1e-13, 2 * max(n, 1) * 2.0**-53)
     assert abs(got - ref) <= bound * abs(ref), f"{what}: grad scale {got!r} vs {ref!r}"
     return bool(np.float32(got) == np.float32(ref))
+
+
+def f16_probe_bits(n_random: int = 2_000_000, seed: int = 11) -> np.ndarray:
+    """fp32 bit patterns on and next to every binary16 rounding boundary (exact ties, one fp32 ulp either
+    side, the overflow threshold, the subnormal range), the specials, and random patterns; both signs."""
+    h = np.arange(0, 0x7C00, dtype=np.uint32)  # every finite non-negative half
+    vals = h.astype(np.uint16).view(np.float16).astype(np.float64)
+    nxt = np.append(vals[1:], 65536.0)
+    mb = ((vals + nxt) / 2).astype(np.float32).view(np.uint32)  # halfway points are exact in fp32
+    base = np.concatenate([mb, mb - 1, mb + 1, vals.astype(np.float32).view(np.uint32)])
+    special = np.array([0x477FF000, 0x477FEFFF, 0x477FF001, 0x47800000, 0x7F7FFFFF, 0x33000000, 0x33000001,
+                        0x32FFFFFF, 0x33C00000, 0x387FE000, 0x387FF000, 0x38800000, 0x00000001, 0x7F800000,
+                        0x7FC00000, 0x7F800001, 0x7FFFFFFF], dtype=np.uint32)
+    rng = np.random.default_rng(seed)
+    rand = rng.integers(0, 2**32, n_random, dtype=np.uint64).astype(np.uint32)
+    near = rng.integers(0x2F000000, 0x48000000, n_random // 2, dtype=np.uint64).astype(np.uint32)
+    allb = np.concatenate([base, special, rand, near])
+    return np.concatenate([allb, allb | 0x80000000])

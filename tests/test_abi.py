@@ -33,19 +33,21 @@ def test_every_declared_symbol_is_exported():
 
 def test_invalid_arguments_rejected_without_device():
     lib = Z.library()
-    assert lib.zero_adamw_step(None, 0, None, None, None, None, -1, None, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_adamw_step(None, 0, None, None, None, None, 0, -1, None, None) == Z.ZERO_ERR_INVALID
     hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 0)  # step 0 is invalid
-    rc = lib.zero_adamw_step(16, 0, 16, 16, 16, 16, 8, hp, None)
+    rc = lib.zero_adamw_step(16, 0, 16, 16, 16, 16, 0, 8, hp, None)
     assert rc == Z.ZERO_ERR_INVALID and "hyper" in Z.zero_last_error()
     hp = Z.zero_adamw_hparams(1e-3, 1.0, 0.999, 1e-8, 0.0, 1.0, 1)  # beta1 = 1 is invalid
-    assert lib.zero_adamw_step(16, 0, 16, 16, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_adamw_step(16, 0, 16, 16, 16, 16, 0, 8, hp, None) == Z.ZERO_ERR_INVALID
     hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, float("inf"), 1)
-    assert lib.zero_adamw_step(16, 0, 16, 16, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_adamw_step(16, 0, 16, 16, 16, 16, 0, 8, hp, None) == Z.ZERO_ERR_INVALID
     hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 1)
-    assert lib.zero_adamw_step(16, 7, 16, 16, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID  # dtype
-    assert lib.zero_adamw_step(16, 0, 18, 16, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID  # fp32 misaligned
-    assert lib.zero_adamw_step(None, 0, 16, 16, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID
-    assert lib.zero_adamw_step(None, 0, None, None, None, None, 0, hp, None) == Z.ZERO_OK  # n = 0: no-op
+    assert lib.zero_adamw_step(16, 7, 16, 16, 16, 16, 0, 8, hp, None) == Z.ZERO_ERR_INVALID  # dtype
+    assert lib.zero_adamw_step(16, 0, 16, 16, 16, 16, 2, 8, hp, None) == Z.ZERO_ERR_INVALID  # parameter dtype
+    assert "parameter dtype" in Z.zero_last_error()
+    assert lib.zero_adamw_step(16, 0, 18, 16, 16, 16, 0, 8, hp, None) == Z.ZERO_ERR_INVALID  # fp32 misaligned
+    assert lib.zero_adamw_step(None, 0, 16, 16, 16, 16, 0, 8, hp, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_adamw_step(None, 0, None, None, None, None, 0, 0, hp, None) == Z.ZERO_OK  # n = 0: no-op
     assert lib.zero_flatten_grads(None, 3, 0, 16, 8, None) == Z.ZERO_ERR_INVALID
     assert lib.zero_flatten_grads(16, -1, 0, 16, 8, None) == Z.ZERO_ERR_INVALID
     assert lib.zero_flatten_grads(16, 1, 0, 17, 8, None) == Z.ZERO_ERR_INVALID  # odd shard address
@@ -156,9 +158,9 @@ def test_tiled_numel_and_invalid_tiled_args():
     assert Z.zero_state_tiled_numel(T + 1) == 6 * T
     lib = Z.library()
     hp = Z.zero_adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1.0, 1)
-    assert lib.zero_adamw_step_tiled(16, 0, 24, 16, 8, hp, None) == Z.ZERO_ERR_INVALID  # state not 16-B aligned
-    assert lib.zero_adamw_step_tiled(16, 0, None, 16, 8, hp, None) == Z.ZERO_ERR_INVALID
-    assert lib.zero_adamw_step_tiled(17, 0, 16, 16, 8, hp, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_adamw_step_tiled(16, 0, 24, 16, 0, 8, hp, None) == Z.ZERO_ERR_INVALID  # state not 16-B aligned
+    assert lib.zero_adamw_step_tiled(16, 0, None, 16, 0, 8, hp, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_adamw_step_tiled(17, 0, 16, 16, 0, 8, hp, None) == Z.ZERO_ERR_INVALID
     assert lib.zero_state_tile(None, 16, 16, 16, 5, None) == Z.ZERO_ERR_INVALID
     assert lib.zero_state_untile(16, 16, 16, 16, -1, None) == Z.ZERO_ERR_INVALID
     ws = Z.zero_grad_sqnorm_workspace_bytes(100)

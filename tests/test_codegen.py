@@ -1,9 +1,10 @@
 """Code-generation invariants of the HIP library (CPU only: compiles the source
 to gfx950 assembly with the library's own flags and reads it).
 
-* Every vector load and store of the streaming update kernels carries the
-  non-temporal hint: the compiler has been seen to drop it silently for some
-  kernel shapes, which costs the update 13% of its bandwidth on MI355X.
+* Every vector load and store of the streaming update kernels (every
+  gradient and parameter format) carries the non-temporal hint: the compiler
+  has been seen to drop it silently for some kernel shapes, which costs the
+  update 13% of its bandwidth on MI355X.
 * No scalar-cache writes of any kind, and no packed-fp32 arithmetic.
 """
 import os
@@ -43,7 +44,7 @@ def kernels(text):
 def test_streaming_update_accesses_are_nontemporal(asm):
     ks = kernels(asm)
     update = {n: b for n, b in ks.items() if "adamw_tiled_kernel" in n or "adamw_vec_kernel" in n}
-    assert len(update) == 4  # bf16 and fp16 for both layouts
+    assert len(update) == 8  # {bf16, fp16} gradients x {bf16, fp16} parameters, both state layouts
     for name, body in update.items():
         wide = [l for l in body if re.match(r"global_(load|store)_dwordx[24]\b", l)]
         assert len(wide) >= 8, name

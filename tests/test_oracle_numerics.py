@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+from tests.parity import f16_probe_bits
 
 
 # ----------------------------------------------------------------- codecs
@@ -47,28 +48,9 @@ def test_bf16_rne_against_torch():
     assert ((got[nan] & 0x7F80) == 0x7F80).all() and ((got[nan] & 0x7F) != 0).all()
 
 
-def _f16_probe_bits():
-    """Every fp32 pattern that lands on or next to a binary16 rounding boundary (exact ties, one ulp either
-    side, the overflow threshold, the subnormal range), plus random patterns."""
-    h = np.arange(0, 0x7C00, dtype=np.uint32)  # every finite non-negative half
-    vals = h.astype(np.uint16).view(np.float16).astype(np.float64)
-    nxt = np.append(vals[1:], 65536.0)
-    mids = ((vals + nxt) / 2).astype(np.float32)  # exact: halfway points are representable in fp32
-    mb = mids.view(np.uint32)
-    base = np.concatenate([mb, mb - 1, mb + 1, vals.astype(np.float32).view(np.uint32)])
-    special = np.array([0x477FF000, 0x477FEFFF, 0x477FF001, 0x47800000, 0x7F7FFFFF, 0x33000000, 0x33000001,
-                        0x32FFFFFF, 0x33C00000, 0x387FE000, 0x387FF000, 0x38800000, 0x00000001, 0x7F800000,
-                        0x7FC00000, 0x7F800001, 0x7FFFFFFF], dtype=np.uint32)
-    rng = np.random.default_rng(11)
-    rand = rng.integers(0, 2**32, 2_000_000, dtype=np.uint64).astype(np.uint32)
-    small = (rng.integers(0x2F000000, 0x48000000, 1_000_000, dtype=np.uint64)).astype(np.uint32)  # near half range
-    allb = np.concatenate([base, special, rand, small])
-    return np.concatenate([allb, allb | 0x80000000])
-
-
 def test_f16_rne_against_numpy_and_torch():
     """fp32 -> binary16 rounding (fp16 parameter output) against two library routines."""
-    x = _f16_probe_bits().view(np.float32)
+    x = f16_probe_bits().view(np.float32)
     got = oracle.f32_to_f16(x)
     with np.errstate(over="ignore"):
         ref_np = x.astype(np.float16).view(np.uint16)
