@@ -163,6 +163,32 @@ int zero_flatten_grads_sqnorm(const zero_flat_seg* segs_dev, int32_t n_segs, zer
                               int64_t shard_numel, void* ws_dev, size_t ws_bytes, double* sqnorm_dev,
                               int32_t* nonfinite_dev, void* stream);
 
+/* Bucketed norm.  With the shard split into constant-capacity windows
+ * (zero_bucket_segments), each window is flattened as soon as its gradients
+ * exist and leaves its per-workgroup partial square-sums and non-finite flags
+ * side by side with the other windows'; one zero_sqnorm_reduce then folds
+ * them all (fixed order: window by window, workgroup by workgroup), so a
+ * bucket costs one launch.
+ *
+ * zero_flatten_partials_count: partials that zero_flatten_grads_partials
+ * writes for a window of numel elements (0 for numel = 0).  Not monotone in
+ * numel: size a shared partials buffer by summing the counts.
+ *
+ * zero_flatten_grads_partials (device): flattens the window exactly as
+ * zero_flatten_grads does (dst_dev = the window's first shard element) and
+ * writes the window's partials to part_sum_dev[0 .. count) (double, 8-byte
+ * aligned) and part_flag_dev[0 .. count) (uint32, 4-byte aligned).  No final
+ * reduction.
+ *
+ * zero_sqnorm_reduce (device): folds count partials in index order into
+ * *sqnorm_dev and *nonfinite_dev (0 or 1), with the same fixed tree as the
+ * final stage of zero_flatten_grads_sqnorm. */
+int64_t zero_flatten_partials_count(int64_t numel);
+int zero_flatten_grads_partials(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype dt, void* dst_dev,
+                                int64_t numel, double* part_sum_dev, uint32_t* part_flag_dev, void* stream);
+int zero_sqnorm_reduce(const double* part_sum_dev, const uint32_t* part_flag_dev, int64_t count, double* sqnorm_dev,
+                       int32_t* nonfinite_dev, void* stream);
+
 /* ------------------------------------------------------------------ grad norm
  *
  * [G] table "AdamW全局grad_norm": inside optimizer.step() the global L2 norm

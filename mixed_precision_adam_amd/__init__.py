@@ -20,7 +20,7 @@ ZERO_FP16 = 1
 ZERO_OK, ZERO_ERR_INVALID, ZERO_ERR_CAPACITY, ZERO_ERR_HIP = 0, -1, -2, -3
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m mixed_precision_adam_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python mixed_precision_adam_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 
 # PyTorch's HIP runtime must be the one the library binds to (it owns the memory and streams the library
@@ -89,6 +89,10 @@ _lib.zero_cosine_lr.restype = C.c_double
 _lib.zero_adamw_step.argtypes = [_P, C.c_int, _P, _P, _P, _P, C.c_int, C.c_int64, C.POINTER(zero_adamw_hparams),
                                  _P]
 _lib.zero_flatten_grads_sqnorm.argtypes = [_P, C.c_int32, C.c_int, _P, C.c_int64, _P, C.c_size_t, _P, _P, _P]
+_lib.zero_flatten_partials_count.argtypes = [C.c_int64]
+_lib.zero_flatten_partials_count.restype = C.c_int64
+_lib.zero_flatten_grads_partials.argtypes = [_P, C.c_int32, C.c_int, _P, C.c_int64, _P, _P, _P]
+_lib.zero_sqnorm_reduce.argtypes = [_P, _P, C.c_int64, _P, _P, _P]
 _lib.zero_state_tiled_numel.argtypes = [C.c_int64]
 _lib.zero_state_tiled_numel.restype = C.c_int64
 _lib.zero_adamw_step_tiled.argtypes = [_P, C.c_int, _P, _P, C.c_int, C.c_int64, C.POINTER(zero_adamw_hparams), _P]
@@ -111,7 +115,8 @@ class zero_step_state(C.Structure):
 
 # Every symbol include/zero_shard.h declares.
 EXPORTS = ("zero_last_error", "zero_shard_layout", "zero_flatten_plan", "zero_bucket_segments", "zero_flatten_grads",
-           "zero_flatten_grads_sqnorm", "zero_grad_sqnorm_workspace_bytes", "zero_grad_sqnorm", "zero_step_decision",
+           "zero_flatten_grads_sqnorm", "zero_flatten_partials_count", "zero_flatten_grads_partials",
+           "zero_sqnorm_reduce", "zero_grad_sqnorm_workspace_bytes", "zero_grad_sqnorm", "zero_step_decision",
            "zero_clip_coef", "zero_loss_scale_update", "zero_cosine_lr", "zero_adamw_step", "zero_state_tiled_numel",
            "zero_adamw_step_tiled", "zero_state_tile", "zero_state_untile", "zero_step_state_init",
            "zero_step_decision_dev", "zero_adamw_step_dev", "zero_adamw_step_tiled_dev")
@@ -257,6 +262,21 @@ def zero_flatten_grads_sqnorm(segs_dev, n_segs: int, dtype: int, shard, shard_nu
                               sqnorm_out, nonfinite_out, stream=None) -> None:
     _check(_lib.zero_flatten_grads_sqnorm(_addr(segs_dev), n_segs, dtype, _addr(shard), shard_numel, _addr(ws),
                                           ws_bytes, _addr(sqnorm_out), _addr(nonfinite_out), _stream(stream)))
+
+
+def zero_flatten_partials_count(numel: int) -> int:
+    return int(_lib.zero_flatten_partials_count(numel))
+
+
+def zero_flatten_grads_partials(segs_dev, n_segs: int, dtype: int, dst, numel: int, part_sum, part_flag,
+                                stream=None) -> None:
+    _check(_lib.zero_flatten_grads_partials(_addr(segs_dev), n_segs, dtype, _addr(dst), numel, _addr(part_sum),
+                                            _addr(part_flag), _stream(stream)))
+
+
+def zero_sqnorm_reduce(part_sum, part_flag, count: int, sqnorm_out, nonfinite_out, stream=None) -> None:
+    _check(_lib.zero_sqnorm_reduce(_addr(part_sum), _addr(part_flag), count, _addr(sqnorm_out), _addr(nonfinite_out),
+                                   _stream(stream)))
 
 
 def zero_state_tiled_numel(n: int) -> int:

@@ -763,6 +763,23 @@ int flatten_args_ok(const char* fn, const zero_flat_seg* segs_dev, int32_t n_seg
   return ZERO_OK;
 }
 
+// The fused flatten with its per-workgroup partial square-sums and flags
+// written to part_sum[0 .. blocks) / part_bad[0 .. blocks).
+int launch_flatten_partials(const char* fn, const zero_flat_seg* segs_dev, int32_t n_segs, int dt, void* dst_dev,
+                            int64_t numel, double* part_sum, uint32_t* part_bad, hipStream_t st) {
+  if (numel <= 0) return ZERO_OK;
+  const int64_t per = flatten_per_block(numel);
+  const int64_t blocks = (numel + per - 1) / per;
+  if (dt == ZERO_BF16) {
+    hipLaunchKernelGGL((flatten_kernel<ZERO_BF16, true>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st,
+                       segs_dev, n_segs, static_cast<uint16_t*>(dst_dev), numel, per, part_sum, part_bad);
+  } else {
+    hipLaunchKernelGGL((flatten_kernel<ZERO_FP16, true>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st,
+                       segs_dev, n_segs, static_cast<uint16_t*>(dst_dev), numel, per, part_sum, part_bad);
+  }
+  return launch_status(fn);
+}
+
 int norm_outputs_ok(const char* fn, int64_t n, const void* ws_dev, size_t ws_bytes, const double* sqnorm_dev,
                     const int32_t* nonfinite_dev) {
   if (!sqnorm_dev || !nonfinite_dev || !ws_dev) return fail(ZERO_ERR_INVALID, "%s: NULL output or workspace", fn);
@@ -890,25 +907,44 @@ int zero_flatten_grads_sqnorm(const zero_flat_seg* segs_dev, int32_t n_segs, zer
   if (rc != ZERO_OK) return rc;
   rc = norm_outputs_ok("zero_flatten_grads_sqnorm", shard_numel, ws_dev, ws_bytes, sqnorm_dev, nonfinite_dev);
   if (rc != ZERO_OK) return rc;
-  const int64_t per = flatten_per_block(shard_numel);
-  const int64_t blocks = shard_numel > 0 ? (shard_numel + per - 1) / per : 0;
+  const int64_t blocks = zero_flatten_partials_count(shard_numel);
   double* part_sum = static_cast<double*>(ws_dev);
   uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sum + (blocks > 0 ? blocks : 1));
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (blocks > 0) {
-    if (dt == ZERO_BF16) {
-      hipLaunchKernelGGL((flatten_kernel<ZERO_BF16, true>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st,
-                         segs_dev, n_segs, static_cast<uint16_t*>(shard_dev), shard_numel, per, part_sum, part_bad);
-    } else {
-      hipLaunchKernelGGL((flatten_kernel<ZERO_FP16, true>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st,
-                         segs_dev, n_segs, static_cast<uint16_t*>(shard_dev), shard_numel, per, part_sum, part_bad);
-    }
-    rc = launch_status("zero_flatten_grads_sqnorm (flatten)");
-    if (rc != ZERO_OK) return rc;
-  }
+  rc = launch_flatten_partials("zero_flatten_grads_sqnorm (flatten)", segs_dev, n_segs, dt, shard_dev, shard_numel,
+                               part_sum, part_bad, st);
+  if (rc != ZERO_OK) return rc;
   hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kBlock), 0, st, part_sum, part_bad, blocks, sqnorm_dev,
                      nonfinite_dev);
   return launch_status("zero_flatten_grads_sqnorm (final)");
+}
+
+int64_t zero_flatten_partials_count(int64_t numel) {
+  if (numel <= 0) return 0;
+  const int64_t per = flatten_per_block(numel);
+  return (numel + per - 1) / per;
+}
+
+int zero_flatten_grads_partials(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype dt, void* dst_dev,
+                                int64_t numel, double* part_sum_dev, uint32_t* part_flag_dev, void* stream) {
+  int rc = flatten_args_ok("zero_flatten_grads_partials", segs_dev, n_segs, dt, dst_dev, numel);
+  if (rc != ZERO_OK) return rc;
+  if (numel > 0 && (!part_sum_dev || !part_flag_dev || !aligned8(part_sum_dev) ||
+                    (reinterpret_cast<uintptr_t>(part_flag_dev) & 3u) != 0))
+    return fail(ZERO_ERR_INVALID, "zero_flatten_grads_partials: partial outputs NULL or misaligned");
+  return launch_flatten_partials("zero_flatten_grads_partials", segs_dev, n_segs, dt, dst_dev, numel, part_sum_dev,
+                                 part_flag_dev, static_cast<hipStream_t>(stream));
+}
+
+int zero_sqnorm_reduce(const double* part_sum_dev, const uint32_t* part_flag_dev, int64_t count, double* sqnorm_dev,
+                       int32_t* nonfinite_dev, void* stream) {
+  if (count < 0 || (count > 0 && (!part_sum_dev || !part_flag_dev)) || !sqnorm_dev || !nonfinite_dev ||
+      !aligned8(sqnorm_dev) || (reinterpret_cast<uintptr_t>(nonfinite_dev) & 3u) != 0 ||
+      (count > 0 && (!aligned8(part_sum_dev) || (reinterpret_cast<uintptr_t>(part_flag_dev) & 3u) != 0)))
+    return fail(ZERO_ERR_INVALID, "zero_sqnorm_reduce: bad arguments");
+  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kBlock), 0, static_cast<hipStream_t>(stream), part_sum_dev,
+                     part_flag_dev, count, sqnorm_dev, nonfinite_dev);
+  return launch_status("zero_sqnorm_reduce");
 }
 
 size_t zero_grad_sqnorm_workspace_bytes(int64_t n) {

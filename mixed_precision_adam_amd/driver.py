@@ -16,7 +16,8 @@ import torch
 from . import (ZERO_BF16, ZERO_FP16, ZERO_STATE_TILE, read_step_state, zero_adamw_step, zero_adamw_step_dev,
                zero_bucket_segments,
                zero_adamw_step_tiled, zero_adamw_step_tiled_dev, zero_flatten_grads, zero_flatten_grads_sqnorm,
-               zero_flatten_plan, zero_grad_sqnorm, zero_grad_sqnorm_workspace_bytes, zero_shard_layout,
+               zero_flatten_grads_partials, zero_flatten_partials_count, zero_flatten_plan, zero_grad_sqnorm,
+               zero_grad_sqnorm_workspace_bytes, zero_shard_layout, zero_sqnorm_reduce,
                zero_state_tile, zero_state_tiled_numel, zero_state_untile, zero_step_decision, zero_step_decision_dev,
                zero_step_state_init)
 
@@ -200,25 +201,27 @@ class DeviceDecision:
 
 class BucketPipeline:
     """Constant-capacity buckets for one rank's shard: as backward produces gradients (last tensors first),
-    each bucket of at most `bucket_numel` shard elements is flattened and square-normed on the compute stream
-    as soon as its source tensors are ready, overlapping with the production of the next bucket.  The per-bucket
-    partials land in their own slots; the device decision sums them in bucket order and the update runs over
-    the whole shard.  The bucket capacity is fixed: it does not grow with the model."""
+    each bucket of at most `bucket_numel` shard elements is flattened on the compute stream as soon as its
+    source tensors are ready, overlapping with the production of the next bucket, and leaves its partial
+    square-sums and flags in its own slice of one partials buffer.  One reduction folds them all (window
+    order), the device decision follows, and the update runs over the whole shard (clipping needs the global
+    norm first).  The bucket capacity is fixed: it does not grow with the model."""
 
     def __init__(self, shard: "RankShard", sources, bucket_numel: int, cfg: AdamWConfig, loss_scale: float = 1.0,
                  growth_interval: int = 2**31 - 1):
-        assert shard.fused, "the pipeline flattens and square-norms each bucket in one pass"
         assert bucket_numel > 0 and bucket_numel % 8 == 0, "whole 16-byte vectors per bucket"
         self.sh = shard
         self.cfg = cfg
         self.sources = sources
         n = shard.n
         self.windows = [(a, min(n, a + bucket_numel)) for a in range(0, n, bucket_numel)] or [(0, 0)]
-        k = len(self.windows)
         dev = shard.device
-        self.norms = torch.zeros(k + (k + 1) // 2, dtype=torch.float64, device=dev)
-        self.sq_base = self.norms.data_ptr()
-        self.flag_base = self.sq_base + 8 * k
+        counts = [zero_flatten_partials_count(b - a) for a, b in self.windows]
+        self.part_first = np.cumsum([0] + counts).tolist()  # window k owns partials [first[k], first[k+1])
+        total = max(self.part_first[-1], 1)
+        self.part_sum = torch.zeros(total, dtype=torch.float64, device=dev)
+        self.part_flag = torch.zeros(total, dtype=torch.int32, device=dev)
+        self.norms = torch.zeros(2, dtype=torch.float64, device=dev)  # the rank's square-norm, then its flag
         self.tables, self.counts, self.tensors = [], [], []
         for a, b in self.windows:
             segs = zero_bucket_segments(shard.segments, a, b - a)
@@ -254,18 +257,21 @@ class BucketPipeline:
         self.sh.adamw_dev(self.state, stream)
 
     def reduce_bucket(self, k: int, stream=None) -> None:
-        """Flatten + square-norm partial of bucket k into its own slot."""
+        """Flatten of bucket k, leaving its partial square-sums and flags in its slice of the partials."""
         sh = self.sh
         a, b = self.windows[k]
-        zero_flatten_grads_sqnorm(self.tables[k], self.counts[k], sh.grad_dtype, sh.grad.data_ptr() +
-                                  a * sh.grad.element_size(), b - a, sh.ws, sh.ws_bytes, self.sq_base + 8 * k,
-                                  self.flag_base + 4 * k, stream)
+        f = self.part_first[k]
+        zero_flatten_grads_partials(self.tables[k], self.counts[k], sh.grad_dtype, sh.grad.data_ptr() +
+                                    a * sh.grad.element_size(), b - a, self.part_sum.data_ptr() + 8 * f,
+                                    self.part_flag.data_ptr() + 4 * f, stream)
 
     def decide(self, stream=None) -> None:
-        """The device decision over the per-bucket partials (summed in bucket order)."""
+        """Folds every bucket's partials (window order), then the device decision."""
         c = self.cfg
-        zero_step_decision_dev(self.sq_base, self.flag_base, len(self.windows), c.max_norm, self.state, lr=c.lr,
-                               beta1=c.beta1, beta2=c.beta2, eps=c.eps, weight_decay=c.weight_decay, stream=stream)
+        sq, fl = self.norms.data_ptr(), self.norms.data_ptr() + 8
+        zero_sqnorm_reduce(self.part_sum, self.part_flag, self.part_first[-1], sq, fl, stream)
+        zero_step_decision_dev(sq, fl, 1, c.max_norm, self.state, lr=c.lr, beta1=c.beta1, beta2=c.beta2, eps=c.eps,
+                               weight_decay=c.weight_decay, stream=stream)
 
     def read(self) -> dict:
         return read_step_state(self.state)

@@ -197,3 +197,18 @@ def test_bucket_segments_cover_the_shard_once():
     assert Z.zero_bucket_segments(segs, 10, 0) == [] and Z.zero_bucket_segments(segs, 3, 0) == []
     with pytest.raises(Exception):
         Z.zero_bucket_segments(segs, -1, 4)
+
+
+
+def test_flatten_partials_count_is_not_monotone():
+    """A 2^25-element bucket runs more flatten workgroups (partials) than a 194.7M-element shard: a shared
+    partials buffer is sized by summing the windows' counts."""
+    n = 194_701_400
+    assert Z.zero_flatten_partials_count(1 << 25) > Z.zero_flatten_partials_count(n)
+    assert Z.zero_flatten_partials_count(0) == 0 and Z.zero_flatten_partials_count(1) == 1
+    for m in (1, 8191, 8192, 8193, 1 << 25, n, 10**10):
+        c = Z.zero_flatten_partials_count(m)
+        assert c >= 1 and Z.zero_grad_sqnorm_workspace_bytes(m) >= c * 12
+    lib = Z.library()
+    assert lib.zero_sqnorm_reduce(None, None, 4, 16, 16, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_flatten_grads_partials(16, 1, 0, 16, 8, None, None, None) == Z.ZERO_ERR_INVALID

@@ -26,9 +26,11 @@ SMALL = [5, 17, 3, 40, 11, 1, 64]  # Ψ = 141: ragged everywhere
 @pytest.mark.parametrize("model,world,rank,bucket", [("gpt2", 2, 0, 65536), ("gpt2", 2, 1, 65536),
                                                      ("gpt2", 3, 2, 1024), ("gpt2", 1, 0, 1 << 24),
                                                      ("gpt2", 2, 1, 100_000), ("small", 2, 1, 8),
-                                                     ("small", 3, 0, 16)])
+                                                     ("small", 3, 0, 16), ("big", 1, 0, 1 << 25)])
 def test_bucket_pipeline_against_oracle(model, world, rank, bucket):
-    numels = gpt2_tensors(d=128, layers=3, vocab=1000, ctx=64, ffn=512)[1] if model == "gpt2" else SMALL
+    numels = {"gpt2": gpt2_tensors(d=128, layers=3, vocab=1000, ctx=64, ffn=512)[1], "small": SMALL,
+              # 40M elements in 2^25 buckets: a bucket runs more flatten blocks than the whole shard would
+              "big": [24_000_001, 16_000_000]}[model]
     psi = sum(numels)
     starts = np.cumsum([0] + numels)
     srcs = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for n in numels]
@@ -69,3 +71,24 @@ def test_bucket_pipeline_against_oracle(model, world, rank, bucket):
         nd += assert_bf16_within_ulp(sh.param.view(torch.int16).cpu().numpy().view(np.uint16), ref[3], "param")
         assert nd == 0 or not same, (t, nd)
 
+
+
+def test_sqnorm_reduce_exact_on_integers_and_flags():
+    """Integer partials below 2^40 sum exactly in any order: the fold must return the exact total; any set
+    flag must give nonfinite = 1; zero partials give (0, 0)."""
+    rng = np.random.default_rng(5)
+    out = torch.zeros(2, dtype=torch.float64, device=DEV)
+    sq, fl = out.data_ptr(), out.data_ptr() + 8
+    for count in (0, 1, 255, 256, 257, 5000, 100_000):
+        vals = rng.integers(0, 2**40, max(count, 1)).astype(np.float64)[:count]
+        ps = torch.from_numpy(np.append(vals, 0.0)).to(DEV)
+        flags = np.zeros(count + 1, np.int32)
+        pf = torch.from_numpy(flags).to(DEV)
+        Z.zero_sqnorm_reduce(ps, pf, count, sq, fl)
+        got = out.cpu().numpy()
+        assert got[0] == float(sum(int(v) for v in vals)), count
+        assert got[1:].view(np.int32)[0] == 0
+        if count:
+            flags[count // 2] = 7
+            Z.zero_sqnorm_reduce(ps, torch.from_numpy(flags).to(DEV), count, sq, fl)
+            assert out.cpu().numpy()[1:].view(np.int32)[0] == 1
