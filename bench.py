@@ -72,8 +72,9 @@ def copy_calibration(nbytes: int, reps: int = 10) -> None:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from the committed counter record, or None when there is no record
-    for this kernel and workload or the kernel source has changed since the counters were taken."""
+    """HBM bytes per update call of `kernel` (all of its launches) from the committed counter record, or None
+    when there is no record for this kernel and workload or the kernel source has changed since the
+    counters were taken."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
@@ -84,7 +85,7 @@ def measured_traffic(kernel: str, workload: str):
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if rec.get("source_sha256") != sha:
         return None
-    return rec["bytes_per_launch"]
+    return rec.get("bytes_per_call")
 
 
 def cpu_baseline(w, sample: int, steps: int) -> dict:
@@ -316,6 +317,7 @@ def main():
             "frac": adam_gbs / HBM_PEAK_GBS,
             "traffic": measured_traffic("adamw_tiled_kernel" if sh.tiled else "adamw_vec_kernel", w.name),
             "bytes_per_param": ADAM_BYTES_PER_PARAM,
+            "per": "update call: the shard in launches of at most 2^25 elements, timed together",
         },
         "breakdown": {
             "adamw_ms": ms["adamw"],

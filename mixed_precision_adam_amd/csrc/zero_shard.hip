@@ -181,7 +181,8 @@ __device__ __forceinline__ void adam_partial4(const uint16_t* __restrict__ grad,
   }
 }
 
-// Separate master / m / v arrays.  Unit u of workgroup b covers elements
+// Separate master / m / v arrays.  Unit u of workgroup b (= block0 + the
+// launch's blockIdx.x) covers elements
 // 4·(b·U·256 + u·256 + t) .. +3 for thread t, so every load and store
 // instruction of a wavefront touches one contiguous span (1 KiB for the fp32
 // arrays, 512 B for grads and params).  All loads of the workgroup's U units
@@ -191,9 +192,10 @@ template <int DT, int PT, int U>
 __global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const uint16_t* __restrict__ grad16,
                                                            float* __restrict__ master, float* __restrict__ mom,
                                                            float* __restrict__ var, uint16_t* __restrict__ param16,
-                                                           int64_t n, AdamScalars s, const zero_step_state* dev) {
+                                                           int64_t n, int64_t block0, AdamScalars s,
+                                                           const zero_step_state* dev) {
   const int64_t n4 = n >> 2;
-  const int64_t first = static_cast<int64_t>(blockIdx.x) * (kBlock * U) + threadIdx.x;
+  const int64_t first = (block0 + blockIdx.x) * (kBlock * U) + threadIdx.x;
   const u32x2* grad = reinterpret_cast<const u32x2*>(grad16);
   f32x4* p4 = reinterpret_cast<f32x4*>(master);
   f32x4* m4 = reinterpret_cast<f32x4*>(mom);
@@ -233,7 +235,7 @@ constexpr int kAdamUnroll = 2;
 // Tiled optimizer state (ZERO_STATE_TILE = 1024 elements per tile): tile k
 // stores master, m and v of elements [1024k, 1024k+1024) back to back, so the
 // update streams three address ranges (grad, state, param) instead of five.
-// One 256-thread workgroup per tile; thread t owns the group of four elements
+// One 256-thread workgroup per tile (tile0 + blockIdx.x); thread t owns the group of four elements
 // 4t .. 4t+3 (kTileUnits groups in general, issuing every load before any
 // arithmetic).  Measured on MI355X, one group per thread and 12 KiB of state
 // per workgroup beats two groups / 24 KiB by 4%, provided every store carries
@@ -249,8 +251,9 @@ template <int DT, int PT>
 __global__ __launch_bounds__(kBlock) void adamw_tiled_kernel(const uint16_t* __restrict__ grad16,
                                                              f32x4* __restrict__ state,
                                                              uint16_t* __restrict__ param16, int64_t n,
-                                                             AdamScalars s, const zero_step_state* dev) {
-  const int64_t tile = blockIdx.x;
+                                                             int64_t tile0, AdamScalars s,
+                                                             const zero_step_state* dev) {
+  const int64_t tile = tile0 + blockIdx.x;
   f32x4* base = state + tile * (3 * kTile4);
   u32x2 g[kTileUnits];
   f32x4 p[kTileUnits], m[kTileUnits], v[kTileUnits];
@@ -598,6 +601,17 @@ int adam_args_ok(const char* fn, const void* grad_dev, int gdt, const void* para
   return ZERO_OK;
 }
 
+// The update is issued in launches of at most 2^25 elements (32768 tiles).
+// Measured on MI355X (tiled state, bf16): one launch over a 3.25e9-element
+// shard sustains 5.58 TB/s and over a 1.95e8-element shard 6.10 TB/s, while
+// launches of 2^24 / 2^25 / 2^26 / 2^27 elements give 6.32 / 6.39 / 6.33 /
+// 6.20 TB/s at every shard size.  Over a long grid the workgroups of the
+// eight XCDs drift apart in the address space; a launch boundary brings
+// them back together at the cost of one drain.
+constexpr int64_t kUpdateElemsPerLaunch = int64_t(1) << 25;
+static_assert(kUpdateElemsPerLaunch % kTile == 0 && kUpdateElemsPerLaunch % (4 * kBlock * kAdamUnroll) == 0,
+              "launches cover whole tiles / whole workgroups");
+
 // Calls f(Formats<G, P>{}) for the run-time (gradient, parameter) format pair,
 // so each launcher names its kernel template once.
 template <int G, int P>
@@ -642,12 +656,18 @@ int launch_adamw_arrays(const char* fn, const void* grad_dev, int gdt, float* ma
   constexpr int64_t per = kBlock * kAdamUnroll;
   const int64_t groups = (n + 3) / 4;  // the last one may be partial
   const int64_t blocks = (groups + per - 1) / per;
-  with_formats(gdt, pdt, [&](auto fm) {
-    using FM = decltype(fm);
-    hipLaunchKernelGGL((adamw_vec_kernel<FM::grad, FM::param, kAdamUnroll>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(kBlock), 0, st, g, master_dev, m_dev, v_dev, param_dev, n, s, dev);
-  });
-  return launch_status(fn);
+  constexpr int64_t kBlocksPerLaunch = kUpdateElemsPerLaunch / (4 * per);
+  for (int64_t b0 = 0; b0 < blocks; b0 += kBlocksPerLaunch) {
+    const int64_t cnt = std::min(kBlocksPerLaunch, blocks - b0);
+    with_formats(gdt, pdt, [&](auto fm) {
+      using FM = decltype(fm);
+      hipLaunchKernelGGL((adamw_vec_kernel<FM::grad, FM::param, kAdamUnroll>), dim3(static_cast<unsigned>(cnt)),
+                         dim3(kBlock), 0, st, g, master_dev, m_dev, v_dev, param_dev, n, b0, s, dev);
+    });
+    const int rc = launch_status(fn);
+    if (rc != ZERO_OK) return rc;
+  }
+  return ZERO_OK;
 }
 
 int launch_adamw_tiled(const char* fn, const void* grad_dev, int gdt, float* state_dev, uint16_t* param_dev, int pdt,
@@ -660,12 +680,18 @@ int launch_adamw_tiled(const char* fn, const void* grad_dev, int gdt, float* sta
     return launch_elements<true>(g, gdt, state_dev, state_dev, state_dev, param_dev, pdt, 0, n, s, dev, st, fn);
   const int64_t tiles = (n + kTile - 1) / kTile;
   auto* state = reinterpret_cast<f32x4*>(state_dev);
-  with_formats(gdt, pdt, [&](auto fm) {
-    using FM = decltype(fm);
-    hipLaunchKernelGGL((adamw_tiled_kernel<FM::grad, FM::param>), dim3(static_cast<unsigned>(tiles)), dim3(kBlock), 0,
-                       st, g, state, param_dev, n, s, dev);
-  });
-  return launch_status(fn);
+  constexpr int64_t kTilesPerLaunch = kUpdateElemsPerLaunch / kTile;
+  for (int64_t t0 = 0; t0 < tiles; t0 += kTilesPerLaunch) {
+    const int64_t cnt = std::min(kTilesPerLaunch, tiles - t0);
+    with_formats(gdt, pdt, [&](auto fm) {
+      using FM = decltype(fm);
+      hipLaunchKernelGGL((adamw_tiled_kernel<FM::grad, FM::param>), dim3(static_cast<unsigned>(cnt)), dim3(kBlock), 0,
+                         st, g, state, param_dev, n, t0, s, dev);
+    });
+    const int rc = launch_status(fn);
+    if (rc != ZERO_OK) return rc;
+  }
+  return ZERO_OK;
 }
 
 int dev_args_ok(const char* fn, const void* grad_dev, int gdt, const void* param_dev, int pdt, int64_t n,

@@ -40,6 +40,9 @@ def windows(layout, segments):
     starts = {0, max(0, (s - WIN) // TILE * TILE)}
     for sg in segments[1:]:
         starts.add(max(0, (sg.dst_offset - WIN // 2) // TILE * TILE))
+    launch = 1 << 25  # the update is issued in launches of this many elements: sample their seams
+    for k in range(1, min(4, s // launch) + 1):
+        starts.add(max(0, (k * launch - WIN // 2) // TILE * TILE))
     for k in range(16):
         h = (k * 0x9E3779B97F4A7C15 + 0x632BE59BD9B4E019) % (1 << 64)
         starts.add((h % max(1, s // TILE)) * TILE)

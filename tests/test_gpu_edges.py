@@ -340,6 +340,17 @@ def test_adamw_tiled_unaligned_grad_param(off):
     _tiled_case(5 * Z.ZERO_STATE_TILE + 3, 0, off, HP_SETS[1], 2, off)
 
 
+@pytest.mark.parametrize("layout", ["arrays", "tiled"])
+def test_adamw_across_launch_boundaries(layout):
+    """Shards longer than one launch (2^25 elements) are updated in several launches: a ragged shard that
+    spans two of them, element by element against the oracle."""
+    n = (1 << 25) + 4096 + 3
+    if layout == "arrays":
+        _adam_case(n, 0, 0, HP_SETS[1], 2, 77)
+    else:
+        _tiled_case(n, 0, 0, HP_SETS[1], 2, 78)
+
+
 def test_tiled_matches_separate_arrays_bitwise():
     n = 300_001
     rng = np.random.default_rng(31)
