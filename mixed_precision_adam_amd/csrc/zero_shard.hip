@@ -423,14 +423,34 @@ __global__ __launch_bounds__(kBlock) void sqnorm_partial_kernel(const uint16_t* 
   }
 }
 
-// Stage 2: one workgroup folds the partials in a fixed order.
+// Stage 2: one workgroup folds the partials in a fixed order: thread t adds
+// partials t, t + 256, t + 512, ... in ascending order, then the workgroup
+// tree.  Loads are issued kR at a time ahead of the additions (the order of
+// the additions is unchanged), so a thread waits on memory once per kR
+// partials instead of once per partial.
 __global__ __launch_bounds__(kBlock) void sqnorm_final_kernel(const double* __restrict__ part_sum,
                                                               const uint32_t* __restrict__ part_bad, int64_t parts,
                                                               double* __restrict__ out_sum,
                                                               int32_t* __restrict__ out_bad) {
+  constexpr int kR = 8;
   double acc = 0.0;
   uint32_t bad = 0;
-  for (int64_t j = threadIdx.x; j < parts; j += kBlock) {
+  int64_t j = threadIdx.x;
+  for (; j + (kR - 1) * kBlock < parts; j += kR * kBlock) {
+    double x[kR];
+    uint32_t f[kR];
+#pragma unroll
+    for (int u = 0; u < kR; ++u) {
+      x[u] = part_sum[j + u * kBlock];
+      f[u] = part_bad[j + u * kBlock];
+    }
+#pragma unroll
+    for (int u = 0; u < kR; ++u) {
+      acc = acc + x[u];
+      bad |= f[u];
+    }
+  }
+  for (; j < parts; j += kBlock) {
     acc = acc + part_sum[j];
     bad |= part_bad[j];
   }
