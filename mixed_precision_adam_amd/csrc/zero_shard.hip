@@ -582,11 +582,18 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(const zero_flat_seg* __
   }
 }
 
-int64_t flatten_per_block(int64_t shard_numel) {
-  constexpr int64_t kMin = 8192, kTargetBlocks = 4096;
-  int64_t per = (shard_numel + kTargetBlocks - 1) / kTargetBlocks;
-  per = (per + kMin - 1) / kMin * kMin;
-  return per < kMin ? kMin : per;
+// Every flatten workgroup owns 8192 shard elements (one pass of four 16-byte
+// vectors per thread).  Measured on MI355X against a fixed grid of 4096
+// workgroups with longer ranges: the Llama-13B rank shard (3.25e9 elements)
+// flattens at 5.6-5.7 instead of 5.1 TB/s, the GPT-2 1.5B one at the same
+// rate, and the whole step gains 0.7-2%.  Past 2^19 workgroups (inputs above
+// 4.3e9 elements) the ranges grow instead, which bounds the partials (the
+// norm workspace) at 6 MiB.
+constexpr int64_t kFlattenPer = 8192, kFlattenMaxBlocks = int64_t(1) << 19;
+int64_t flatten_per_block(int64_t n) {
+  int64_t per = (n + kFlattenMaxBlocks - 1) / kFlattenMaxBlocks;
+  per = (per + kFlattenPer - 1) / kFlattenPer * kFlattenPer;
+  return per < kFlattenPer ? kFlattenPer : per;
 }
 
 bool dtype_ok(int dt) { return dt == ZERO_BF16 || dt == ZERO_FP16; }

@@ -63,8 +63,15 @@ def test_invalid_arguments_rejected_without_device():
 
 
 def test_workspace_size_is_bounded():
+    """At most 2^19 partials of 12 bytes (6 MiB) whatever the size; one 8192-element range per partial up to
+    4.3e9 elements."""
     assert Z.zero_grad_sqnorm_workspace_bytes(0) == 256
-    assert Z.zero_grad_sqnorm_workspace_bytes(10**12) <= 64 * 1024
+    cap = 12 * (1 << 19)
+    for n in (10**9, 3_253_966_080, 1 << 32, 10**10, 10**12, 2**62):
+        assert Z.zero_grad_sqnorm_workspace_bytes(n) <= cap, n
+        assert Z.zero_flatten_partials_count(n) <= 1 << 19, n
+    assert Z.zero_flatten_partials_count(3_253_966_080) == -(-3_253_966_080 // 8192)
+    assert Z.zero_flatten_partials_count(194_701_400) == -(-194_701_400 // 8192)
 
 
 def _same_layout(numels, world, rank):
@@ -201,10 +208,10 @@ def test_bucket_segments_cover_the_shard_once():
 
 
 def test_flatten_partials_count_is_not_monotone():
-    """A 2^25-element bucket runs more flatten workgroups (partials) than a 194.7M-element shard: a shared
-    partials buffer is sized by summing the windows' counts."""
-    n = 194_701_400
-    assert Z.zero_flatten_partials_count(1 << 25) > Z.zero_flatten_partials_count(n)
+    """Past 2^19 partials the flatten's ranges grow, so a 2^32-element window can run more workgroups
+    (partials) than a larger one: a shared partials buffer is sized by summing the windows' counts."""
+    n = 5_000_000_000  # past 2^19 ranges of 8192 the ranges grow
+    assert Z.zero_flatten_partials_count(1 << 32) > Z.zero_flatten_partials_count(n)
     assert Z.zero_flatten_partials_count(0) == 0 and Z.zero_flatten_partials_count(1) == 1
     for m in (1, 8191, 8192, 8193, 1 << 25, n, 10**10):
         c = Z.zero_flatten_partials_count(m)

@@ -29,7 +29,7 @@ SMALL = [5, 17, 3, 40, 11, 1, 64]  # Ψ = 141: ragged everywhere
                                                      ("small", 3, 0, 16), ("big", 1, 0, 1 << 25)])
 def test_bucket_pipeline_against_oracle(model, world, rank, bucket):
     numels = {"gpt2": gpt2_tensors(d=128, layers=3, vocab=1000, ctx=64, ffn=512)[1], "small": SMALL,
-              # 40M elements in 2^25 buckets: a bucket runs more flatten blocks than the whole shard would
+              # 40M elements in two 2^25-element buckets, the capacity the benchmark uses
               "big": [24_000_001, 16_000_000]}[model]
     psi = sum(numels)
     starts = np.cumsum([0] + numels)
