@@ -180,13 +180,15 @@ int zero_flatten_grads_sqnorm(const zero_flat_seg* segs_dev, int32_t n_segs, zer
  * aligned) and part_flag_dev[0 .. count) (uint32, 4-byte aligned).  No final
  * reduction.
  *
- * zero_sqnorm_reduce (device): folds count partials in index order into
- * *sqnorm_dev and *nonfinite_dev (0 or 1), with the same fixed tree as the
- * final stage of zero_flatten_grads_sqnorm. */
+ * zero_sqnorm_reduce (device): folds count partials into *sqnorm_dev and
+ * *nonfinite_dev (0 or 1) in a fixed order (deterministic for a given
+ * count), exactly as zero_flatten_grads_sqnorm folds its own.  Past 65536
+ * partials the fold takes two levels and overwrites the partials: they are
+ * scratch once reduced. */
 int64_t zero_flatten_partials_count(int64_t numel);
 int zero_flatten_grads_partials(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype dt, void* dst_dev,
                                 int64_t numel, double* part_sum_dev, uint32_t* part_flag_dev, void* stream);
-int zero_sqnorm_reduce(const double* part_sum_dev, const uint32_t* part_flag_dev, int64_t count, double* sqnorm_dev,
+int zero_sqnorm_reduce(double* part_sum_dev, uint32_t* part_flag_dev, int64_t count, double* sqnorm_dev,
                        int32_t* nonfinite_dev, void* stream);
 
 /* ------------------------------------------------------------------ grad norm

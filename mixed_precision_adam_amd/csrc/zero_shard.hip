@@ -363,11 +363,12 @@ __device__ __forceinline__ void accumulate8(u32x4 w, double& acc, uint32_t& bad)
   }
 }
 
-// Sum over the workgroup in a fixed tree: butterfly inside each wavefront,
-// then the four wavefront sums in order.  Result valid in thread 0.
+// Sum over a workgroup of NT threads in a fixed tree: butterfly inside each
+// wavefront, then the NT/64 wavefront sums in order.  Result valid in thread 0.
+template <int NT = kBlock>
 __device__ __forceinline__ void block_reduce(double& acc, uint32_t& bad) {
-  __shared__ double wsum[kBlock / 64];
-  __shared__ uint32_t wbad[kBlock / 64];
+  __shared__ double wsum[NT / 64];
+  __shared__ uint32_t wbad[NT / 64];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     acc = acc + __shfl_xor(acc, off, 64);
@@ -383,7 +384,7 @@ __device__ __forceinline__ void block_reduce(double& acc, uint32_t& bad) {
     acc = wsum[0];
     bad = wbad[0];
 #pragma unroll
-    for (int w = 1; w < kBlock / 64; ++w) {
+    for (int w = 1; w < NT / 64; ++w) {
       acc = acc + wsum[w];
       bad |= wbad[w];
     }
@@ -423,26 +424,29 @@ __global__ __launch_bounds__(kBlock) void sqnorm_partial_kernel(const uint16_t* 
   }
 }
 
-// Stage 2: one workgroup folds the partials in a fixed order: thread t adds
-// partials t, t + 256, t + 512, ... in ascending order, then the workgroup
-// tree.  Loads are issued kR at a time ahead of the additions (the order of
-// the additions is unchanged), so a thread waits on memory once per kR
-// partials instead of once per partial.
-__global__ __launch_bounds__(kBlock) void sqnorm_final_kernel(const double* __restrict__ part_sum,
-                                                              const uint32_t* __restrict__ part_bad, int64_t parts,
-                                                              double* __restrict__ out_sum,
-                                                              int32_t* __restrict__ out_bad) {
+// Stage 2: one workgroup of kFoldThreads folds `parts` partials, read at
+// indices 0, stride, 2·stride, ..., in a fixed order: thread t adds partials
+// t, t + kFoldThreads, ... in ascending order, then the workgroup tree.  It is
+// bound by memory latency: loads are issued kR at a time ahead of the
+// additions (which keep their order), and 16 wavefronts keep 16 times more
+// of them in flight than one.
+constexpr int kFoldThreads = 1024;
+__global__ __launch_bounds__(kFoldThreads) void sqnorm_final_kernel(const double* __restrict__ part_sum,
+                                                                    const uint32_t* __restrict__ part_bad,
+                                                                    int64_t parts, int64_t stride,
+                                                                    double* __restrict__ out_sum,
+                                                                    int32_t* __restrict__ out_bad) {
   constexpr int kR = 8;
   double acc = 0.0;
   uint32_t bad = 0;
   int64_t j = threadIdx.x;
-  for (; j + (kR - 1) * kBlock < parts; j += kR * kBlock) {
+  for (; j + (kR - 1) * kFoldThreads < parts; j += kR * kFoldThreads) {
     double x[kR];
     uint32_t f[kR];
 #pragma unroll
     for (int u = 0; u < kR; ++u) {
-      x[u] = part_sum[j + u * kBlock];
-      f[u] = part_bad[j + u * kBlock];
+      x[u] = part_sum[(j + u * kFoldThreads) * stride];
+      f[u] = part_bad[(j + u * kFoldThreads) * stride];
     }
 #pragma unroll
     for (int u = 0; u < kR; ++u) {
@@ -450,14 +454,49 @@ __global__ __launch_bounds__(kBlock) void sqnorm_final_kernel(const double* __re
       bad |= f[u];
     }
   }
-  for (; j < parts; j += kBlock) {
-    acc = acc + part_sum[j];
-    bad |= part_bad[j];
+  for (; j < parts; j += kFoldThreads) {
+    acc = acc + part_sum[j * stride];
+    bad |= part_bad[j * stride];
   }
-  block_reduce(acc, bad);
+  block_reduce<kFoldThreads>(acc, bad);
   if (threadIdx.x == 0) {
     *out_sum = acc;
     *out_bad = bad ? 1 : 0;
+  }
+}
+
+// A single workgroup reads its partials at the bandwidth of one compute unit:
+// 397,213 partials (the flatten of a 3.25e9-element shard) took 96 us.  Past
+// kFoldTwoLevel partials the fold therefore takes two levels: workgroup g
+// folds the chunk [g·kFoldChunk, (g+1)·kFoldChunk) in a fixed order (thread
+// t adds the chunk's partials t, t + 256, ... in order, then the workgroup
+// tree) and leaves the result in place of the chunk's first partial, which it
+// has already read; stage 2 then folds those at stride kFoldChunk.  The
+// partials buffer is scratch and is overwritten.
+constexpr int64_t kFoldChunk = 4096, kFoldTwoLevel = 65536;
+__global__ __launch_bounds__(kBlock) void sqnorm_fold_chunks_kernel(double* __restrict__ part_sum,
+                                                                    uint32_t* __restrict__ part_bad, int64_t parts) {
+  constexpr int kPer = static_cast<int>(kFoldChunk / kBlock);
+  const int64_t lo = static_cast<int64_t>(blockIdx.x) * kFoldChunk;
+  double x[kPer];
+  uint32_t f[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int64_t j = lo + threadIdx.x + u * kBlock;
+    x[u] = j < parts ? part_sum[j] : 0.0;  // adding +0.0 to a sum of non-negative terms changes nothing
+    f[u] = j < parts ? part_bad[j] : 0u;
+  }
+  double acc = 0.0;
+  uint32_t bad = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    acc = acc + x[u];
+    bad |= f[u];
+  }
+  block_reduce(acc, bad);  // its barrier orders every read of the chunk before the write below
+  if (threadIdx.x == 0) {
+    part_sum[lo] = acc;
+    part_bad[lo] = bad;
   }
 }
 
@@ -833,6 +872,25 @@ int launch_flatten_partials(const char* fn, const zero_flat_seg* segs_dev, int32
   return launch_status(fn);
 }
 
+// Folds `parts` partials (overwriting them when it takes two levels) into
+// *out_sum and *out_bad.
+int launch_fold(const char* fn, double* part_sum, uint32_t* part_bad, int64_t parts, double* out_sum,
+                int32_t* out_bad, hipStream_t st) {
+  int64_t count = parts, stride = 1;
+  if (parts > kFoldTwoLevel) {
+    const int64_t chunks = (parts + kFoldChunk - 1) / kFoldChunk;
+    hipLaunchKernelGGL(sqnorm_fold_chunks_kernel, dim3(static_cast<unsigned>(chunks)), dim3(kBlock), 0, st, part_sum,
+                       part_bad, parts);
+    const int rc = launch_status(fn);
+    if (rc != ZERO_OK) return rc;
+    count = chunks;
+    stride = kFoldChunk;
+  }
+  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kFoldThreads), 0, st, part_sum, part_bad, count, stride,
+                     out_sum, out_bad);
+  return launch_status(fn);
+}
+
 int norm_outputs_ok(const char* fn, int64_t n, const void* ws_dev, size_t ws_bytes, const double* sqnorm_dev,
                     const int32_t* nonfinite_dev) {
   if (!sqnorm_dev || !nonfinite_dev || !ws_dev) return fail(ZERO_ERR_INVALID, "%s: NULL output or workspace", fn);
@@ -967,9 +1025,7 @@ int zero_flatten_grads_sqnorm(const zero_flat_seg* segs_dev, int32_t n_segs, zer
   rc = launch_flatten_partials("zero_flatten_grads_sqnorm (flatten)", segs_dev, n_segs, dt, shard_dev, shard_numel,
                                part_sum, part_bad, st);
   if (rc != ZERO_OK) return rc;
-  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kBlock), 0, st, part_sum, part_bad, blocks, sqnorm_dev,
-                     nonfinite_dev);
-  return launch_status("zero_flatten_grads_sqnorm (final)");
+  return launch_fold("zero_flatten_grads_sqnorm (fold)", part_sum, part_bad, blocks, sqnorm_dev, nonfinite_dev, st);
 }
 
 int64_t zero_flatten_partials_count(int64_t numel) {
@@ -989,15 +1045,14 @@ int zero_flatten_grads_partials(const zero_flat_seg* segs_dev, int32_t n_segs, z
                                  part_flag_dev, static_cast<hipStream_t>(stream));
 }
 
-int zero_sqnorm_reduce(const double* part_sum_dev, const uint32_t* part_flag_dev, int64_t count, double* sqnorm_dev,
+int zero_sqnorm_reduce(double* part_sum_dev, uint32_t* part_flag_dev, int64_t count, double* sqnorm_dev,
                        int32_t* nonfinite_dev, void* stream) {
   if (count < 0 || (count > 0 && (!part_sum_dev || !part_flag_dev)) || !sqnorm_dev || !nonfinite_dev ||
       !aligned8(sqnorm_dev) || (reinterpret_cast<uintptr_t>(nonfinite_dev) & 3u) != 0 ||
       (count > 0 && (!aligned8(part_sum_dev) || (reinterpret_cast<uintptr_t>(part_flag_dev) & 3u) != 0)))
     return fail(ZERO_ERR_INVALID, "zero_sqnorm_reduce: bad arguments");
-  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kBlock), 0, static_cast<hipStream_t>(stream), part_sum_dev,
-                     part_flag_dev, count, sqnorm_dev, nonfinite_dev);
-  return launch_status("zero_sqnorm_reduce");
+  return launch_fold("zero_sqnorm_reduce", part_sum_dev, part_flag_dev, count, sqnorm_dev, nonfinite_dev,
+                     static_cast<hipStream_t>(stream));
 }
 
 size_t zero_grad_sqnorm_workspace_bytes(int64_t n) {
@@ -1036,9 +1091,7 @@ int zero_grad_sqnorm(const void* shard_dev, zero_dtype dt, int64_t n, void* ws_d
   }
   rc = launch_status("zero_grad_sqnorm (partials)");
   if (rc != ZERO_OK) return rc;
-  hipLaunchKernelGGL(sqnorm_final_kernel, dim3(1), dim3(kBlock), 0, st, part_sum, part_bad, parts, sqnorm_dev,
-                     nonfinite_dev);
-  return launch_status("zero_grad_sqnorm (final)");
+  return launch_fold("zero_grad_sqnorm (fold)", part_sum, part_bad, parts, sqnorm_dev, nonfinite_dev, st);
 }
 
 double zero_clip_coef(double global_sqnorm, double max_norm) {

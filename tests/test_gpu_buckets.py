@@ -74,13 +74,15 @@ def test_bucket_pipeline_against_oracle(model, world, rank, bucket):
 
 
 def test_sqnorm_reduce_exact_on_integers_and_flags():
-    """Integer partials below 2^40 sum exactly in any order: the fold must return the exact total; any set
-    flag must give nonfinite = 1; zero partials give (0, 0)."""
+    """Integer partials whose total stays below 2^53 (at most 397,213 values below 2^33) sum exactly in any
+    order: the fold must return the exact total, with one level and with two (past 65,536 partials, where
+    the partials are overwritten); any set flag must give nonfinite = 1; zero partials give (0, 0)."""
     rng = np.random.default_rng(5)
     out = torch.zeros(2, dtype=torch.float64, device=DEV)
     sq, fl = out.data_ptr(), out.data_ptr() + 8
-    for count in (0, 1, 255, 256, 257, 5000, 100_000):
-        vals = rng.integers(0, 2**40, max(count, 1)).astype(np.float64)[:count]
+    for count in (0, 1, 255, 256, 257, 5000, 65_536, 65_537, 100_000, 4096 * 40, 397_213):
+        vals = rng.integers(0, 2**33, max(count, 1)).astype(np.float64)[:count]
+        assert sum(int(v) for v in vals) < 2**53
         ps = torch.from_numpy(np.append(vals, 0.0)).to(DEV)
         flags = np.zeros(count + 1, np.int32)
         pf = torch.from_numpy(flags).to(DEV)
@@ -89,6 +91,8 @@ def test_sqnorm_reduce_exact_on_integers_and_flags():
         assert got[0] == float(sum(int(v) for v in vals)), count
         assert got[1:].view(np.int32)[0] == 0
         if count:
-            flags[count // 2] = 7
-            Z.zero_sqnorm_reduce(ps, torch.from_numpy(flags).to(DEV), count, sq, fl)
-            assert out.cpu().numpy()[1:].view(np.int32)[0] == 1
+            for at in (count // 2, count - 1, 0):
+                flags[:] = 0
+                flags[at] = 7
+                Z.zero_sqnorm_reduce(ps, torch.from_numpy(flags).to(DEV), count, sq, fl)
+                assert out.cpu().numpy()[1:].view(np.int32)[0] == 1, (count, at)
