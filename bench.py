@@ -130,8 +130,8 @@ def cpu_baseline(w, sample: int, steps: int) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(multi-GPU sharding is a design note, not part of this build)", file=sys.stderr)
+        print(f"bench.py measures one rank's step on one GPU; --gpus {args.gpus} is not supported: the library "
+              "has no collectives, and how the step shards over GPUs is described, not implemented", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)

@@ -1,10 +1,12 @@
 """Comparison helpers shared by the GPU parity tests (no method arithmetic).
 
-Tolerances (stated by the task this library is held to):
-  * layout, offsets, flatten copies, the non-finite flag: bit-exact;
-  * fp32 master / m / v: |gpu - oracle| <= 1e-6 · |oracle| per element (zeros must match exactly);
-  * bf16 param: within 1 ulp (adjacent bf16 values);
-  * gradient square-norm: within 1e-5 relative of the fp64 oracle.
+Tolerances:
+  * layout, offsets, flatten copies, the non-finite flag: bit-exact (integer and byte work);
+  * fp32 master / m / v: |gpu - oracle| <= 1e-6 · |oracle| per element (zeros must match exactly); every
+    element is one fixed sequence of correctly rounded fp32 operations, so equality is expected;
+  * 16-bit param (bf16 or fp16): within 1 ulp (adjacent values);
+  * gradient square-norm: within 1e-5 relative of the fp64 oracle, and within the 2n·2^-53 bound of two
+    fp64 summation orders.
 """
 from __future__ import annotations
 
