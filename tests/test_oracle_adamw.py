@@ -120,6 +120,23 @@ def test_step1_closed_form(hi):
     np.testing.assert_allclose(v, (1 - hp["beta2"]) * g * g, rtol=1e-6)
 
 
+def test_four_element_worked_example():
+    """A four-element, two-step example worked out beforehand, step by step in numpy float32 from the same
+    reading (lr 1e-3, betas (0.9, 0.999), eps 1e-8, wd 0.01, no clipping, p0 = [1, -2, 0.5, 0], gradients
+    [0.1, -0.2, 0, 3] then [0.05, 0.2, -0.3, -3]).  That example used fp32 gradients; here they are rounded to
+    bf16 first, which leaves every master bit of both steps unchanged at these hyper-parameters (the update
+    depends on the gradients through m / sqrt(v), which a common 0.1% rounding barely moves)."""
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    p = np.array([1.0, -2.0, 0.5, 0.0], np.float32)
+    m, v, q = np.zeros(4, np.float32), np.zeros(4, np.float32), np.zeros(4, np.uint16)
+    expect = [[0x3F7FBDCF, 0xBFFFDE93, 0x3EFFFF58, 0xBA83126E], [0x3F7F8010, 0xBFFFDFA5, 0x3F00301D, 0xBA785824]]
+    for t, g in enumerate(([0.1, -0.2, 0.0, 3.0], [0.05, 0.2, -0.3, -3.0]), start=1):
+        oracle.adamw_step(oracle.f32_to_bf16(np.array(g, np.float32)), oracle.BF16, p, m, v, q, grad_scale=1.0,
+                          step=t, **hp)
+        assert p.view(np.uint32).tolist() == expect[t - 1], (t, [hex(x) for x in p.view(np.uint32)])
+    assert q[3] == 0xBA78
+
+
 def test_lr_zero_leaves_master_bits():
     master0, grads = _inputs(1000, 2, 5, [1.0, 1.0])
     p, m, v, q = _run_oracle(master0, grads, dict(lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.5),
