@@ -41,14 +41,22 @@
 extern "C" {
 #endif
 
+/* Element counts are limited to 2^58 (ZERO_MAX_NUMEL): larger counts are
+ * rejected with ZERO_ERR_INVALID, and the size queries return 0 for them. */
+#define ZERO_MAX_NUMEL (INT64_MAX / 32)
+
 enum {
   ZERO_OK = 0,
-  ZERO_ERR_INVALID = -1,  /* bad argument (null pointer, negative size, rank out of range, ...) */
+  ZERO_ERR_INVALID = -1,  /* bad argument (null pointer, negative or too large size, rank out of range, ...) */
   ZERO_ERR_CAPACITY = -2, /* caller-provided array too small; the required count is returned */
   ZERO_ERR_HIP = -3       /* the HIP runtime rejected a launch */
 };
 
-typedef enum { ZERO_BF16 = 0, ZERO_FP16 = 1 } zero_dtype;
+/* 16-bit floating-point formats.  Passed as a plain int32_t (an enum's size
+ * and value range are implementation-defined across C and C++); any other
+ * value is rejected with ZERO_ERR_INVALID. */
+typedef int32_t zero_dtype;
+enum { ZERO_BF16 = 0, ZERO_FP16 = 1 };
 
 /* Message describing the calling thread's most recent failure ("" if none). */
 const char* zero_last_error(void);

@@ -44,7 +44,11 @@ int launch_status(const char* what) {
   return ZERO_OK;
 }
 
-constexpr int64_t kMaxPsi = std::numeric_limits<int64_t>::max() / 32;  // 2^58: keeps 16·Ψ and N·S in range
+constexpr int64_t kMaxPsi = ZERO_MAX_NUMEL;  // 2^58: keeps 16·Ψ and N·S in range
+static_assert(kMaxPsi == std::numeric_limits<int64_t>::max() / 32, "element-count limit");
+
+// ceil(a / b) for a >= 0, b > 0, without forming a + b - 1 (which can overflow).
+constexpr int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0 ? 1 : 0); }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -339,7 +343,7 @@ constexpr int64_t kNormElemsPerPart = int64_t(1) << 16;
 constexpr int64_t kNormMaxParts = 4096;
 
 int64_t norm_parts(int64_t n) {
-  int64_t parts = (n + kNormElemsPerPart - 1) / kNormElemsPerPart;
+  int64_t parts = ceil_div(n, kNormElemsPerPart);
   if (parts < 1) parts = 1;
   if (parts > kNormMaxParts) parts = kNormMaxParts;
   return parts;
@@ -630,8 +634,8 @@ __global__ __launch_bounds__(kBlock) void flatten_kernel(const zero_flat_seg* __
 // norm workspace) at 6 MiB.
 constexpr int64_t kFlattenPer = 8192, kFlattenMaxBlocks = int64_t(1) << 19;
 int64_t flatten_per_block(int64_t n) {
-  int64_t per = (n + kFlattenMaxBlocks - 1) / kFlattenMaxBlocks;
-  per = (per + kFlattenPer - 1) / kFlattenPer * kFlattenPer;
+  int64_t per = ceil_div(n, kFlattenMaxBlocks);
+  per = ceil_div(per, kFlattenPer) * kFlattenPer;
   return per < kFlattenPer ? kFlattenPer : per;
 }
 
@@ -644,7 +648,7 @@ int adam_args_ok(const char* fn, const void* grad_dev, int gdt, const void* para
   if (!dtype_ok(gdt)) return fail(ZERO_ERR_INVALID, "%s: unknown dtype %d", fn, gdt);
   if (!dtype_ok(pdt)) return fail(ZERO_ERR_INVALID, "%s: unknown parameter dtype %d", fn, pdt);
   if (!hp) return fail(ZERO_ERR_INVALID, "%s: hparams NULL", fn);
-  if (n < 0) return fail(ZERO_ERR_INVALID, "%s: n < 0", fn);
+  if (n < 0 || n > kMaxPsi) return fail(ZERO_ERR_INVALID, "%s: n = %lld out of range", fn, static_cast<long long>(n));
   if (n > 0 && (!grad_dev || !param_dev)) return fail(ZERO_ERR_INVALID, "%s: NULL grad or param", fn);
   if (hp->step < 1 || !(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0) ||
       !(hp->eps >= 0.0) || !(hp->lr >= 0.0) || !(hp->weight_decay >= 0.0) || !std::isfinite(hp->grad_scale) ||
@@ -698,7 +702,7 @@ int launch_elements(const uint16_t* grad, int gdt, float* master, float* m, floa
                     int64_t begin, int64_t n, const AdamScalars& s, const zero_step_state* dev, hipStream_t st,
                     const char* what) {
   if (begin >= n) return ZERO_OK;
-  const int64_t blocks = std::min<int64_t>((n - begin + kBlock - 1) / kBlock, 65536);
+  const int64_t blocks = std::min<int64_t>(ceil_div(n - begin, kBlock), 65536);
   with_formats(gdt, pdt, [&](auto fm) {
     using FM = decltype(fm);
     hipLaunchKernelGGL((adamw_element_kernel<FM::grad, FM::param, TILED>), dim3(static_cast<unsigned>(blocks)),
@@ -721,7 +725,7 @@ int launch_adamw_arrays(const char* fn, const void* grad_dev, int gdt, float* ma
   if (!vec) return launch_elements<false>(g, gdt, master_dev, m_dev, v_dev, param_dev, pdt, 0, n, s, dev, st, fn);
   constexpr int64_t per = kBlock * kAdamUnroll;
   const int64_t groups = (n + 3) / 4;  // the last one may be partial
-  const int64_t blocks = (groups + per - 1) / per;
+  const int64_t blocks = ceil_div(groups, per);
   constexpr int64_t kBlocksPerLaunch = kUpdateElemsPerLaunch / (4 * per);
   for (int64_t b0 = 0; b0 < blocks; b0 += kBlocksPerLaunch) {
     const int64_t cnt = std::min(kBlocksPerLaunch, blocks - b0);
@@ -744,7 +748,7 @@ int launch_adamw_tiled(const char* fn, const void* grad_dev, int gdt, float* sta
   const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
   if (!aligned8(grad_dev) || !aligned8(param_dev))
     return launch_elements<true>(g, gdt, state_dev, state_dev, state_dev, param_dev, pdt, 0, n, s, dev, st, fn);
-  const int64_t tiles = (n + kTile - 1) / kTile;
+  const int64_t tiles = ceil_div(n, kTile);
   auto* state = reinterpret_cast<f32x4*>(state_dev);
   constexpr int64_t kTilesPerLaunch = kUpdateElemsPerLaunch / kTile;
   for (int64_t t0 = 0; t0 < tiles; t0 += kTilesPerLaunch) {
@@ -765,7 +769,7 @@ int dev_args_ok(const char* fn, const void* grad_dev, int gdt, const void* param
   if (!dtype_ok(gdt)) return fail(ZERO_ERR_INVALID, "%s: unknown dtype %d", fn, gdt);
   if (!dtype_ok(pdt)) return fail(ZERO_ERR_INVALID, "%s: unknown parameter dtype %d", fn, pdt);
   if (!dev || !aligned16(dev)) return fail(ZERO_ERR_INVALID, "%s: step state NULL or not 16-byte aligned", fn);
-  if (n < 0) return fail(ZERO_ERR_INVALID, "%s: n < 0", fn);
+  if (n < 0 || n > kMaxPsi) return fail(ZERO_ERR_INVALID, "%s: n = %lld out of range", fn, static_cast<long long>(n));
   if (n > 0 && (!grad_dev || !param_dev)) return fail(ZERO_ERR_INVALID, "%s: NULL grad or param", fn);
   if (((reinterpret_cast<uintptr_t>(grad_dev) | reinterpret_cast<uintptr_t>(param_dev)) & 1u) != 0)
     return fail(ZERO_ERR_INVALID, "%s: 16-bit buffers not 2-byte aligned", fn);
@@ -846,7 +850,7 @@ int flatten_args_ok(const char* fn, const zero_flat_seg* segs_dev, int32_t n_seg
   if (!dtype_ok(dt)) return fail(ZERO_ERR_INVALID, "%s: unknown dtype %d", fn, dt);
   if (n_segs < 0 || (n_segs > 0 && !segs_dev))
     return fail(ZERO_ERR_INVALID, "%s: bad segment table (n_segs=%d)", fn, n_segs);
-  if (shard_numel < 0 || (shard_numel > 0 && !shard_dev))
+  if (shard_numel < 0 || shard_numel > kMaxPsi || (shard_numel > 0 && !shard_dev))
     return fail(ZERO_ERR_INVALID, "%s: bad shard (numel=%lld)", fn, static_cast<long long>(shard_numel));
   if ((reinterpret_cast<uintptr_t>(shard_dev) & 1u) != 0)
     return fail(ZERO_ERR_INVALID, "%s: shard must be 2-byte aligned", fn);
@@ -861,7 +865,7 @@ int launch_flatten_partials(const char* fn, const zero_flat_seg* segs_dev, int32
                             int64_t numel, double* part_sum, uint32_t* part_bad, hipStream_t st) {
   if (numel <= 0) return ZERO_OK;
   const int64_t per = flatten_per_block(numel);
-  const int64_t blocks = (numel + per - 1) / per;
+  const int64_t blocks = ceil_div(numel, per);
   if (dt == ZERO_BF16) {
     hipLaunchKernelGGL((flatten_kernel<ZERO_BF16, true>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0, st,
                        segs_dev, n_segs, static_cast<uint16_t*>(dst_dev), numel, per, part_sum, part_bad);
@@ -878,7 +882,7 @@ int launch_fold(const char* fn, double* part_sum, uint32_t* part_bad, int64_t pa
                 int32_t* out_bad, hipStream_t st) {
   int64_t count = parts, stride = 1;
   if (parts > kFoldTwoLevel) {
-    const int64_t chunks = (parts + kFoldChunk - 1) / kFoldChunk;
+    const int64_t chunks = ceil_div(parts, kFoldChunk);
     hipLaunchKernelGGL(sqnorm_fold_chunks_kernel, dim3(static_cast<unsigned>(chunks)), dim3(kBlock), 0, st, part_sum,
                        part_bad, parts);
     const int rc = launch_status(fn);
@@ -924,7 +928,7 @@ int zero_shard_layout(const int64_t* numels, int32_t n_tensors, int32_t world, i
                   static_cast<long long>(numels[t]));
     psi += numels[t];
   }
-  const int64_t shard = (psi + world - 1) / world;
+  const int64_t shard = ceil_div(psi, world);
   const int64_t begin = static_cast<int64_t>(rank) * shard;
   const int64_t stop = begin + shard < psi ? begin + shard : psi;  // end of real (unpadded) elements
   zero_layout L{};
@@ -1004,7 +1008,7 @@ int zero_flatten_grads(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype
   int rc = flatten_args_ok("zero_flatten_grads", segs_dev, n_segs, dt, shard_dev, shard_numel);
   if (rc != ZERO_OK || shard_numel == 0) return rc;
   const int64_t per = flatten_per_block(shard_numel);
-  const int64_t blocks = (shard_numel + per - 1) / per;
+  const int64_t blocks = ceil_div(shard_numel, per);
   hipLaunchKernelGGL((flatten_kernel<ZERO_BF16, false>), dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
                      static_cast<hipStream_t>(stream), segs_dev, n_segs, static_cast<uint16_t*>(shard_dev),
                      shard_numel, per, nullptr, nullptr);
@@ -1031,7 +1035,7 @@ int zero_flatten_grads_sqnorm(const zero_flat_seg* segs_dev, int32_t n_segs, zer
 int64_t zero_flatten_partials_count(int64_t numel) {
   if (numel <= 0) return 0;
   const int64_t per = flatten_per_block(numel);
-  return (numel + per - 1) / per;
+  return ceil_div(numel, per);
 }
 
 int zero_flatten_grads_partials(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype dt, void* dst_dev,
@@ -1047,8 +1051,8 @@ int zero_flatten_grads_partials(const zero_flat_seg* segs_dev, int32_t n_segs, z
 
 int zero_sqnorm_reduce(double* part_sum_dev, uint32_t* part_flag_dev, int64_t count, double* sqnorm_dev,
                        int32_t* nonfinite_dev, void* stream) {
-  if (count < 0 || (count > 0 && (!part_sum_dev || !part_flag_dev)) || !sqnorm_dev || !nonfinite_dev ||
-      !aligned8(sqnorm_dev) || (reinterpret_cast<uintptr_t>(nonfinite_dev) & 3u) != 0 ||
+  if (count < 0 || count > kMaxPsi || (count > 0 && (!part_sum_dev || !part_flag_dev)) || !sqnorm_dev ||
+      !nonfinite_dev || !aligned8(sqnorm_dev) || (reinterpret_cast<uintptr_t>(nonfinite_dev) & 3u) != 0 ||
       (count > 0 && (!aligned8(part_sum_dev) || (reinterpret_cast<uintptr_t>(part_flag_dev) & 3u) != 0)))
     return fail(ZERO_ERR_INVALID, "zero_sqnorm_reduce: bad arguments");
   return launch_fold("zero_sqnorm_reduce", part_sum_dev, part_flag_dev, count, sqnorm_dev, nonfinite_dev,
@@ -1058,7 +1062,7 @@ int zero_sqnorm_reduce(double* part_sum_dev, uint32_t* part_flag_dev, int64_t co
 size_t zero_grad_sqnorm_workspace_bytes(int64_t n) {
   if (n < 0) n = 0;
   int64_t parts = norm_parts(n);
-  const int64_t fl = n > 0 ? (n + flatten_per_block(n) - 1) / flatten_per_block(n) : 1;
+  const int64_t fl = n > 0 ? ceil_div(n, flatten_per_block(n)) : 1;
   if (fl > parts) parts = fl;
   const size_t bytes = static_cast<size_t>(parts) * (sizeof(double) + sizeof(uint32_t));
   return (bytes + 255) / 256 * 256;
@@ -1067,7 +1071,7 @@ size_t zero_grad_sqnorm_workspace_bytes(int64_t n) {
 int zero_grad_sqnorm(const void* shard_dev, zero_dtype dt, int64_t n, void* ws_dev, size_t ws_bytes,
                      double* sqnorm_dev, int32_t* nonfinite_dev, void* stream) {
   if (!dtype_ok(dt)) return fail(ZERO_ERR_INVALID, "zero_grad_sqnorm: unknown dtype %d", static_cast<int>(dt));
-  if (n < 0 || (n > 0 && !shard_dev)) return fail(ZERO_ERR_INVALID, "zero_grad_sqnorm: bad shard");
+  if (n < 0 || n > kMaxPsi || (n > 0 && !shard_dev)) return fail(ZERO_ERR_INVALID, "zero_grad_sqnorm: bad shard");
   if ((reinterpret_cast<uintptr_t>(shard_dev) & 1u) != 0)
     return fail(ZERO_ERR_INVALID, "zero_grad_sqnorm: shard must be 2-byte aligned");
   int rc = norm_outputs_ok("zero_grad_sqnorm", n, ws_dev, ws_bytes, sqnorm_dev, nonfinite_dev);
@@ -1077,7 +1081,7 @@ int zero_grad_sqnorm(const void* shard_dev, zero_dtype dt, int64_t n, void* ws_d
   int64_t head = static_cast<int64_t>(((16u - (reinterpret_cast<uintptr_t>(x) & 15u)) & 15u) >> 1);
   if (head > n) head = n;
   const int64_t n8 = (n - head) >> 3;
-  int64_t per = (n8 + parts - 1) / parts;
+  int64_t per = ceil_div(n8, parts);
   if (per < 1) per = 1;
   double* part_sum = static_cast<double*>(ws_dev);
   uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sum + parts);
@@ -1166,8 +1170,8 @@ int zero_adamw_step_dev(const void* grad_dev, zero_dtype gdt, float* master_dev,
 }
 
 int64_t zero_state_tiled_numel(int64_t n) {
-  if (n <= 0) return 0;
-  return 3 * kTile * ((n + kTile - 1) / kTile);
+  if (n <= 0 || n > kMaxPsi) return 0;
+  return 3 * kTile * ceil_div(n, kTile);
 }
 
 int zero_adamw_step_tiled(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev,
@@ -1210,10 +1214,10 @@ int zero_step_decision_dev(const double* rank_sqnorms_dev, const int32_t* rank_f
 
 int zero_state_tile(const float* master_dev, const float* m_dev, const float* v_dev, float* state_dev, int64_t n,
                     void* stream) {
-  if (n < 0 || (n > 0 && (!master_dev || !m_dev || !v_dev || !state_dev)))
+  if (n < 0 || n > kMaxPsi || (n > 0 && (!master_dev || !m_dev || !v_dev || !state_dev)))
     return fail(ZERO_ERR_INVALID, "zero_state_tile: bad arguments");
   if (n == 0) return ZERO_OK;
-  const int64_t blocks = std::min<int64_t>((n + kBlock - 1) / kBlock, 65536);
+  const int64_t blocks = std::min<int64_t>(ceil_div(n, kBlock), 65536);
   hipLaunchKernelGGL(retile_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
                      static_cast<hipStream_t>(stream), const_cast<float*>(master_dev), const_cast<float*>(m_dev),
                      const_cast<float*>(v_dev), state_dev, n);
@@ -1221,10 +1225,10 @@ int zero_state_tile(const float* master_dev, const float* m_dev, const float* v_
 }
 
 int zero_state_untile(const float* state_dev, float* master_dev, float* m_dev, float* v_dev, int64_t n, void* stream) {
-  if (n < 0 || (n > 0 && (!master_dev || !m_dev || !v_dev || !state_dev)))
+  if (n < 0 || n > kMaxPsi || (n > 0 && (!master_dev || !m_dev || !v_dev || !state_dev)))
     return fail(ZERO_ERR_INVALID, "zero_state_untile: bad arguments");
   if (n == 0) return ZERO_OK;
-  const int64_t blocks = std::min<int64_t>((n + kBlock - 1) / kBlock, 65536);
+  const int64_t blocks = std::min<int64_t>(ceil_div(n, kBlock), 65536);
   hipLaunchKernelGGL(retile_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
                      static_cast<hipStream_t>(stream), master_dev, m_dev, v_dev, const_cast<float*>(state_dev), n);
   return launch_status("zero_state_untile");
