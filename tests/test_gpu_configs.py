@@ -176,3 +176,70 @@ def test_config_parity(name):
     assert skips == expect_skips
     if name == "llama-13b":
         assert scaler.scale == 16384.0 and scaler.adam_step == 4
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("bucket", [0, 1 << 25])
+def test_benchmark_path_parity_gpt2(bucket):
+    """The GPT-2 1.5B rank shard exactly as `bench.py` steps it: fused flatten + norm (in one pass, or in
+    constant-capacity buckets of 2^25 elements, last first), the decision on the device, the tiled update in
+    launches of 2^25 elements.  The GPU takes its own decision here; the oracle takes its own, and the states
+    must agree bit for bit whenever the two fp32 factors coincide (within tolerance otherwise)."""
+    from mixed_precision_adam_amd.driver import BucketPipeline, DeviceDecision
+
+    w = WORKLOADS["gpt2-1.5b"]
+    dev = torch.device("cuda:0")
+    rank = w.ranks[0]
+    lay, segs = Z.zero_shard_layout(w.numels, w.world, rank)
+    starts = np.cumsum([0] + list(w.numels))
+    sources = [None] * len(w.numels)
+    for sg in segs:
+        sources[sg.tensor] = torch.empty(w.numels[sg.tensor], dtype=torch.bfloat16, device=dev)
+    sh = RankShard(w.numels, w.world, rank, Z.ZERO_BF16, dev, sources=sources, tiled=True, fused=True)
+    S = sh.n
+    master0 = torch.zeros(S, dtype=torch.float32, device=dev)
+    synth.fill_tensor(w.master_field(), lay.shard_offset, master0[:lay.shard_valid])
+    sh.load_master(master0)
+    del master0
+    cfg = AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, max_norm=w.clip)
+    runner = BucketPipeline(sh, sources, bucket, cfg) if bucket else DeviceDecision([sh], cfg)
+    if bucket:
+        assert len(runner.windows) == -(-S // bucket)
+    wins = windows(lay, segs)
+    if bucket:  # the seams between buckets too
+        wins = sorted(set(wins) | {(max(0, k * bucket - WIN // 2), min(S, k * bucket + WIN // 2))
+                                   for k in range(1, -(-S // bucket))})
+    ref = []
+    for a, b in wins:
+        p = np.zeros(b - a, np.float32)
+        va = min(b, lay.shard_valid)
+        if va > a:
+            synth.fill_host(w.master_field(), lay.shard_offset + a, va - a, out=p[:va - a])
+        ref.append([p, np.zeros(b - a, np.float32), np.zeros(b - a, np.float32), np.zeros(b - a, np.uint16)])
+    torch.cuda.synchronize()
+    for t in range(1, w.steps + 1):
+        print(f"[gpt2 bucket={bucket}] step {t}", flush=True)
+        field = w.grad_field(t)
+        for sg in segs:
+            synth.fill_tensor(field, int(starts[sg.tensor]), sources[sg.tensor])
+        runner.step()
+        st = runner.read()
+        g_host = host_shard_grads(w, field, lay)
+        for a, b in wins:
+            assert_bits_equal(bits16(sh.grad[a:b]), g_host[a:b], f"bucket={bucket} step {t} shard [{a},{b})")
+        osq, oflag = oracle.sqnorm(g_host, Z.ZERO_BF16)
+        od = oracle.step_decision([osq], [oflag], w.clip, 1.0, 0, 2**31 - 1)
+        assert st["skip"] == od["skip"] == 0 and st["adam_step"] == t
+        assert_norm_close(st["global_norm"] ** 2, od["global_norm"] ** 2, S, f"bucket={bucket} step {t} norm")
+        same = assert_grad_scale_close(st["grad_scale"], od["grad_scale"], S, f"bucket={bucket} step {t}")
+        nd = 0
+        for (a, b), R in zip(wins, ref):
+            oracle.adamw_step(g_host[a:b].copy(), Z.ZERO_BF16, R[0], R[1], R[2], R[3], lr=w.lr, beta1=w.beta1,
+                              beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, grad_scale=od["grad_scale"],
+                              step=t)
+            gp, gm, gv = (x.cpu().numpy() for x in sh.state_views(a, b))
+            what = f"bucket={bucket} step {t} [{a},{b})"
+            nd += assert_f32_close(gp, R[0], what + " master") + assert_f32_close(gm, R[1], what + " m")
+            nd += assert_f32_close(gv, R[2], what + " v")
+            nd += assert_bf16_within_ulp(bits16(sh.param[a:b]), R[3], what + " param")
+        assert nd == 0 or not same, f"bucket={bucket} step {t}: {nd} sampled elements differ with equal factors"
