@@ -2,9 +2,12 @@
 
 Holds the device buffers of a simulated data-parallel rank (PyTorch
 allocations) and calls the library entry points in the order of the step:
-flatten -> square-norm -> (simulated all-reduce + decision) -> AdamW.  No
-arithmetic of the method happens here; the decision is the library's
-``zero_step_decision``.
+flatten -> square-norm -> (simulated all-reduce + decision) -> AdamW.  Three
+ways of sequencing it: ``rank_step`` (decision on the host after a 16-byte
+readback), ``DeviceDecision`` (decision on the GPU, nothing waits on the
+host) and ``BucketPipeline`` (flatten + norm partials in constant-capacity
+buckets as gradients arrive on a producer stream).  No arithmetic of the
+method happens here: every step is a library call.
 """
 from __future__ import annotations
 
@@ -14,12 +17,11 @@ import numpy as np
 import torch
 
 from . import (ZERO_BF16, ZERO_FP16, ZERO_STATE_TILE, read_step_state, zero_adamw_step, zero_adamw_step_dev,
-               zero_bucket_segments,
-               zero_adamw_step_tiled, zero_adamw_step_tiled_dev, zero_flatten_grads, zero_flatten_grads_sqnorm,
-               zero_flatten_grads_partials, zero_flatten_partials_count, zero_flatten_plan, zero_grad_sqnorm,
-               zero_grad_sqnorm_workspace_bytes, zero_shard_layout, zero_sqnorm_reduce,
-               zero_state_tile, zero_state_tiled_numel, zero_state_untile, zero_step_decision, zero_step_decision_dev,
-               zero_step_state_init)
+               zero_adamw_step_tiled, zero_adamw_step_tiled_dev, zero_bucket_segments, zero_flatten_grads,
+               zero_flatten_grads_partials, zero_flatten_grads_sqnorm, zero_flatten_partials_count,
+               zero_flatten_plan, zero_grad_sqnorm, zero_grad_sqnorm_workspace_bytes, zero_shard_layout,
+               zero_sqnorm_reduce, zero_state_tile, zero_state_tiled_numel, zero_state_untile, zero_step_decision,
+               zero_step_decision_dev, zero_step_state_init)
 
 _TORCH16 = {ZERO_BF16: torch.bfloat16, ZERO_FP16: torch.float16}
 
