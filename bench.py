@@ -48,6 +48,9 @@ def parse():
                     help="decision on the GPU (no host round trip, default) or on the host after a 16-byte readback")
     ap.add_argument("--bucket", type=int, default=0,
                     help="constant bucket capacity in shard elements (0: one pass over the whole shard)")
+    ap.add_argument("--produce", action="store_true",
+                    help="produce the rank's gradients inside every timed step (the synthetic generator stands in "
+                         "for backward): before the step, or bucket by bucket on a producer stream with --bucket")
     ap.add_argument("--event-every", type=int, default=4,
                     help="bracket the kernels of every k-th timed step with HIP events (each record costs ~3 us)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
@@ -176,6 +179,17 @@ def main():
     scaler = ScalerState(scale=w.loss_scale, growth_interval=growth)
     ddec = DeviceDecision([sh], cfg, loss_scale=w.loss_scale, growth_interval=growth) if args.decision == "device" \
         else None
+    if args.produce:
+        assert args.decision == "device", "--produce needs the device decision"
+    prod_stream = torch.cuda.Stream() if args.produce else None
+    landing_set = set(landing)
+
+    def produce(idx, st):
+        """Writes the gradients of source tensors `idx` (those that land in the shard) on stream `st`."""
+        for t in idx:
+            if t in landing_set:
+                synth.fill_device(gf, starts[t], w.numels[t], sources[t].data_ptr(), st.cuda_stream)
+
     pipe = None
     if args.bucket:
         assert ddec is not None and sh.fused, "the bucketed step uses the fused flatten and the device decision"
@@ -201,10 +215,11 @@ def main():
                                    ctypes.byref(nseg))
         assert rc == 0 and nseg.value == len(segs)
         if pipe is not None:                           # fixed-capacity buckets, last bucket first
+            if args.produce:                           # backward stand-in on the producer stream
+                pipe.launch_production(produce, prod_stream, stream)
             if e:
                 e[0].record(stream)
-            for k in range(len(pipe.windows) - 1, -1, -1):
-                pipe.reduce_bucket(k, stream)          # a2 + a3 of one bucket
+            pipe.reduce_all(stream, wait=args.produce)  # a2 + a3, bucket by bucket
             if e:
                 e[1].record(stream)
             pipe.decide(stream)                        # a4 over the bucket partials
@@ -217,6 +232,8 @@ def main():
                 ev["adamw"].append((e[4], e[5]))
             return None
         if ddec is not None:                           # everything on the GPU, nothing waits on the host
+            if args.produce:                           # backward stand-in, all before the step
+                produce(landing, stream)
             if e:
                 e[0].record(stream)
             sh.flatten(stream)                         # a2 + a3 (fused)
@@ -305,7 +322,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: rank {rank} of N={w.world}, shard {S} params "
-                        f"(psi={lay.psi}, {len(segs)} tensor pieces), {'bf16' if gdt == 0 else 'fp16'} grads",
+                        f"(psi={lay.psi}, {len(segs)} tensor pieces), {'bf16' if gdt == 0 else 'fp16'} grads"
+                        + (", gradients generated inside each step" if args.produce else "")
+                        + (f", flattened in buckets of {args.bucket}" if args.bucket else ""),
             "psi": lay.psi, "world": w.world, "rank": rank, "shard_numel": S, "segments": len(segs),
         },
         "roofline": {
@@ -325,6 +344,7 @@ def main():
             "state_layout": args.state,
             "decision": args.decision,
             "bucket_numel": args.bucket or None,
+            "gradients_produced_in_step": args.produce,
             "buckets": len(pipe.windows) if pipe is not None else None,
             "flatten_norm_fused": sh.fused,
             "flatten_ms": ms["flatten"],

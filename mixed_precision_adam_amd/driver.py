@@ -242,21 +242,28 @@ class BucketPipeline:
         backward); it runs on `producer` in backward order, one bucket at a time, each followed by an event
         the compute stream waits for.  Without `produce` the sources are taken as ready."""
         stream = stream or torch.cuda.current_stream()
-        done = set()
-        order = range(len(self.windows) - 1, -1, -1)
         if produce is not None:
-            producer.wait_stream(stream)  # the previous step has finished reading the sources
-            for k in order:
-                need = [t for t in self.tensors[k] if t not in done]
-                produce(need, producer)
-                done.update(need)
-                self.events[k].record(producer)
-        for k in order:
-            if produce is not None:
-                stream.wait_event(self.events[k])
-            self.reduce_bucket(k, stream)
+            self.launch_production(produce, producer, stream)
+        self.reduce_all(stream, wait=produce is not None)
         self.decide(stream)
         self.sh.adamw_dev(self.state, stream)
+
+    def launch_production(self, produce, producer, stream) -> None:
+        """Queues gradient production on `producer`, last bucket first, with one event per bucket."""
+        producer.wait_stream(stream)  # the previous step has finished reading the sources
+        done = set()
+        for k in range(len(self.windows) - 1, -1, -1):
+            need = [t for t in self.tensors[k] if t not in done]
+            produce(need, producer)
+            done.update(need)
+            self.events[k].record(producer)
+
+    def reduce_all(self, stream=None, wait: bool = False) -> None:
+        """Flatten + norm partials of every bucket, last first; with `wait` each waits for its event."""
+        for k in range(len(self.windows) - 1, -1, -1):
+            if wait:
+                stream.wait_event(self.events[k])
+            self.reduce_bucket(k, stream)
 
     def reduce_bucket(self, k: int, stream=None) -> None:
         """Flatten of bucket k, leaving its partial square-sums and flags in its slice of the partials."""
