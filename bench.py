@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--produce", action="store_true",
                     help="produce the rank's gradients inside every timed step (the synthetic generator stands in "
                          "for backward): before the step, or bucket by bucket on a producer stream with --bucket")
+    ap.add_argument("--producer", choices=("separate", "same"), default="separate",
+                    help="with --produce: generate gradients on their own stream (default) or on the compute stream")
     ap.add_argument("--event-every", type=int, default=4,
                     help="bracket the kernels of every k-th timed step with HIP events (each record costs ~3 us)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
@@ -181,7 +183,9 @@ def main():
         else None
     if args.produce:
         assert args.decision == "device", "--produce needs the device decision"
-    prod_stream = torch.cuda.Stream() if args.produce else None
+    prod_stream = None
+    if args.produce:
+        prod_stream = torch.cuda.Stream() if args.producer == "separate" else torch.cuda.current_stream()
     landing_set = set(landing)
 
     def produce(idx, st):
@@ -345,6 +349,7 @@ def main():
             "decision": args.decision,
             "bucket_numel": args.bucket or None,
             "gradients_produced_in_step": args.produce,
+            "producer_stream": args.producer if args.produce else None,
             "buckets": len(pipe.windows) if pipe is not None else None,
             "flatten_norm_fused": sh.fused,
             "flatten_ms": ms["flatten"],
