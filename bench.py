@@ -94,8 +94,9 @@ def measured_traffic(kernel: str, workload: str):
 
 
 def cpu_baseline(w, sample: int, steps: int) -> dict:
-    """The oracle (single-threaded C), untuned, on the first `sample` elements of the rank's shard:
-    `steps` whole steps (flatten + square-norm + decision + AdamW), timed with a monotonic clock."""
+    """The oracle (single-threaded C), untuned, on the first `sample` elements of the rank's shard (default:
+    all of it up to 2^28 elements): `steps` whole steps (flatten unless the gradients are generated in the
+    shard, square-norm, decision, AdamW), timed with a monotonic clock."""
     import numpy as np
 
     import oracle
@@ -103,7 +104,8 @@ def cpu_baseline(w, sample: int, steps: int) -> dict:
 
     rank = w.ranks[0]
     lay = oracle.layout(w.numels, w.world, rank)
-    sample = min(sample, lay.shard_valid) if sample > 0 else lay.shard_valid
+    sample = min(sample if sample > 0 else 1 << 28, lay.shard_valid)
+    odt = oracle.BF16 if w.grad_kind == synth.BF16 else oracle.FP16
     lo, hi = lay.shard_offset, lay.shard_offset + sample
     numels, tensors = [], []
     start = 0
@@ -120,16 +122,17 @@ def cpu_baseline(w, sample: int, steps: int) -> dict:
     q = np.zeros(sample, np.uint16)
     t0 = time.perf_counter()
     for t in range(1, steps + 1):
-        shard = oracle.flatten(tensors, numels, 1, 0)
-        sq, flag = oracle.sqnorm(shard, oracle.BF16)
-        dec = oracle.step_decision([sq], [flag], w.clip, 1.0, 0, 2**31 - 1)
-        oracle.adamw_step(shard, oracle.BF16, master, m, v, q, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+        shard = tensors[0] if w.flat_shard_only else oracle.flatten(tensors, numels, 1, 0)
+        sq, flag = oracle.sqnorm(shard, odt)
+        dec = oracle.step_decision([sq], [flag], w.clip, w.loss_scale, 0, 2**31 - 1)
+        oracle.adamw_step(shard, odt, master, m, v, q, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                           weight_decay=w.weight_decay, grad_scale=dec["grad_scale"], step=t)
     dt = time.perf_counter() - t0
     return {"value": sample * steps / dt, "unit": "params/s", "cores": 1, "kind": "oracle",
             "sample": f"{'whole' if sample == lay.shard_valid else f'first {sample} params of the'} rank's shard "
-                      f"({sample} params, {len(numels)} tensor pieces), {steps} full steps (flatten + fp64 sqnorm "
-                      f"+ decision + AdamW) on the same gradients, {dt:.2f} s on one host core"}
+                      f"({sample} params, {len(numels)} tensor pieces), {steps} full steps "
+                      f"({'' if w.flat_shard_only else 'flatten + '}fp64 sqnorm + decision + AdamW) on the same "
+                      f"gradients, {dt:.2f} s on one host core"}
 
 
 def main():
@@ -151,7 +154,12 @@ def main():
     from synth.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    assert not w.flat_shard_only, "bench workloads flatten per-tensor gradients"
+    # Gradients generated straight into the shard (the 1T ZeRO-3 shard): no per-tensor sources, no flatten;
+    # the step is square-norm -> decision -> update.
+    flat = w.flat_shard_only
+    if flat:
+        assert not (args.bucket or args.produce or args.unfused) and args.decision == "device", \
+            "a shard-only workload runs the one-pass device path"
     dev = torch.device("cuda:0")
     rank = w.ranks[0]
     torch.cuda.set_device(dev)
@@ -165,12 +173,17 @@ def main():
     dt16 = torch.bfloat16 if w.grad_kind == synth.BF16 else torch.float16
     sources = [None] * len(w.numels)
     gf = w.grad_field(1)
+    if flat:
+        landing = []
     for t in landing:
         sources[t] = torch.empty(w.numels[t], dtype=dt16, device=dev)
         synth.fill_tensor(gf, starts[t], sources[t])
     gdt = Z.ZERO_BF16 if w.grad_kind == synth.BF16 else Z.ZERO_FP16
-    sh = RankShard(w.numels, w.world, rank, gdt, dev, sources=sources, tiled=args.state == "tiled",
-                   fused=not args.unfused)
+    sh = RankShard(w.numels, w.world, rank, gdt, dev, sources=None if flat else sources,
+                   tiled=args.state == "tiled", fused=not (args.unfused or flat))
+    if flat:
+        sh.grad[lay.shard_valid:].zero_()
+        synth.fill_tensor(gf, lay.shard_offset, sh.grad[:lay.shard_valid])
     master0 = torch.zeros(lay.shard_numel, dtype=torch.float32, device=dev)
     synth.fill_tensor(w.master_field(), lay.shard_offset, master0[:lay.shard_valid])
     sh.load_master(master0)
@@ -212,7 +225,12 @@ def main():
     # and the update of every k-th step (a record costs a few microseconds of GPU time)
     pool = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
 
+    count = [0]
+
     def step(e=None):
+        if w.lr_min is not None:  # the workload's cosine schedule, cycled over its step count
+            count[0] += 1
+            cfg.lr = Z.zero_cosine_lr((count[0] - 1) % w.steps + 1, w.steps, w.lr, w.lr_min)
         # a1: layout (host) -- recomputed every step as part of the path
         rc = lib.zero_shard_layout(ctypes.cast(numels_c, ctypes.c_void_p), len(w.numels), w.world, rank,
                                    ctypes.byref(lay_out), ctypes.cast(seg_buf, ctypes.c_void_p), len(segs),
@@ -240,8 +258,9 @@ def main():
                 produce(landing, stream)
             if e:
                 e[0].record(stream)
-            sh.flatten(stream)                         # a2 + a3 (fused)
-            if not sh.fused:
+            if not flat:
+                sh.flatten(stream)                     # a2 + a3 (fused)
+            if flat or not sh.fused:
                 sh.sqnorm(stream)                      # a3
             if e:
                 e[1].record(stream)
@@ -310,7 +329,10 @@ def main():
     adam_gbs = ADAM_BYTES_PER_PARAM * S / (ms["adamw"] * 1e-3) / 1e9
     ms_per_step = elapsed / args.steps * 1e3
     params_per_s = S * args.steps / elapsed
-    step_bpp = ADAM_BYTES_PER_PARAM + FLATTEN_BYTES_PER_PARAM + (0 if sh.fused else NORM_BYTES_PER_PARAM)
+    if flat:
+        step_bpp = ADAM_BYTES_PER_PARAM + NORM_BYTES_PER_PARAM
+    else:
+        step_bpp = ADAM_BYTES_PER_PARAM + FLATTEN_BYTES_PER_PARAM + (0 if sh.fused else NORM_BYTES_PER_PARAM)
     result = {
         "metric": METRIC,
         "value": params_per_s,
@@ -328,6 +350,8 @@ def main():
             "workload": f"{w.name}: rank {rank} of N={w.world}, shard {S} params "
                         f"(psi={lay.psi}, {len(segs)} tensor pieces), {'bf16' if gdt == 0 else 'fp16'} grads"
                         + (", gradients generated inside each step" if args.produce else "")
+                        + (", gradients generated in the shard (no flatten)" if flat else "")
+                        + (", cosine lr" if w.lr_min is not None else "")
                         + (f", flattened in buckets of {args.bucket}" if args.bucket else ""),
             "psi": lay.psi, "world": w.world, "rank": rank, "shard_numel": S, "segments": len(segs),
         },
@@ -352,11 +376,11 @@ def main():
             "producer_stream": args.producer if args.produce else None,
             "buckets": len(pipe.windows) if pipe is not None else None,
             "flatten_norm_fused": sh.fused,
-            "flatten_ms": ms["flatten"],
-            "flatten_gbs": FLATTEN_BYTES_PER_PARAM * S / (ms["flatten"] * 1e-3) / 1e9,
-            "sqnorm_ms": ms["sqnorm"] if ev["sqnorm"] else None,
-            "sqnorm_gbs": (NORM_BYTES_PER_PARAM * S / (ms["sqnorm"] * 1e-3) / 1e9) if ev["sqnorm"] and not sh.fused
-            else None,
+            "flatten_ms": None if flat else ms["flatten"],
+            "flatten_gbs": None if flat else FLATTEN_BYTES_PER_PARAM * S / (ms["flatten"] * 1e-3) / 1e9,
+            "sqnorm_ms": ms["flatten"] if flat else (ms["sqnorm"] if ev["sqnorm"] else None),
+            "sqnorm_gbs": NORM_BYTES_PER_PARAM * S / (ms["flatten" if flat else "sqnorm"] * 1e-3) / 1e9
+            if flat or (ev["sqnorm"] and not sh.fused) else None,
             "step_bytes_per_param": step_bpp,
             "step_gbs_algorithmic": step_bpp * params_per_s / 1e9,
             "last_global_norm": dec["global_norm"],
