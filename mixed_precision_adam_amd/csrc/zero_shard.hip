@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const uint16_t* __res
   }
 }
 
-constexpr int kAdamUnroll = 2;
+constexpr int kAdamUnroll = 1;
 
 // Tiled optimizer state (ZERO_STATE_TILE = 1024 elements per tile): tile k
 // stores master, m and v of elements [1024k, 1024k+1024) back to back, so the

@@ -32,11 +32,12 @@ def asm():
 
 
 def kernels(text):
-    """name -> body (instruction lines) for every kernel in the assembly."""
+    """name -> body (instruction lines) for every kernel in the assembly.  A kernel can have several exits
+    (s_endpgm), so its body runs to its .Lfunc_end label."""
     out = {}
     for m in re.finditer(r"^(_Z\S*):\s*;\s*@", text, re.M):
         name = m.group(1)
-        end = text.index("s_endpgm", m.end())
+        end = text.index(".Lfunc_end", m.end())
         out[name] = [l.strip() for l in text[m.end():end].splitlines() if re.match(r"\s+[a-z_]+\d*", l)]
     return out
 
