@@ -65,17 +65,31 @@ typedef struct {
   float b1, omb1, b2, omb2, eps, decay, step_size, bc2_sqrt, gscale;
 } orc_scalars;
 
-/* Layout of rank `rank` of `world` over the flat concatenation of the tensors. */
+/* Layout of rank `rank` of `world` over the flat concatenation of the tensors.
+ * Pinned to: the per-rank memory figures the pages print ([X] section 三,
+ * [Z] section 八, [O]), their other algebraic forms, the 8-parameter /
+ * 4-GPU example ([Z] section 六（二）), the communication volumes of [Z]
+ * section 六, and brute-force coverage of every Ψ <= 64, N <= 9. */
 int orc_layout_compute(const int64_t* numels, int32_t n_tensors, int32_t world, int32_t rank,
                        orc_layout* out, orc_segment* segs, int32_t segs_cap, int32_t* n_segs);
 
-/* shard[j] = flat[rank·S + j] for flat index < Ψ, else +0 (bit copy). */
+/* shard[j] = flat[rank·S + j] for flat index < Ψ, else +0 (bit copy).
+ * Pinned to: numpy concatenation and slicing (the definition), the
+ * 8-parameter example. */
 int orc_flatten(const uint16_t* const* tensors, const int64_t* numels, int32_t n_tensors,
                 int32_t world, int32_t rank, uint16_t* shard);
 
-/* Σ x_j² accumulated in fp64 in index order; nonfinite = any all-ones exponent. */
+/* Σ x_j² accumulated in fp64 in index order; nonfinite = any all-ones exponent.
+ * Pinned to: exact rational sums within the sequential rounding bound, hand
+ * vectors, numpy and torch fp64, inf/NaN patterns of both formats. */
 int orc_sqnorm(const uint16_t* x, int32_t dtype, int64_t n, double* sqnorm, int32_t* nonfinite);
 
+/* Clip coefficient, loss-scale update and the decision that composes them
+ * (reading of [G]: torch clip_grad_norm_ and GradScaler conventions).
+ * Pinned to: torch clip_grad_norm_ and torch's loss-scale update on the CPU;
+ * overflow skips and halves.  The cosine rate: pinned to torch's
+ * CosineAnnealingLR closed form.  The policies themselves are readings the
+ * pages do not fix (parity unpinned by the pages). */
 double orc_clip_coef(double global_sqnorm, double max_norm);
 int orc_loss_scale_update(double* scale, int32_t nonfinite, int32_t* good_steps, int32_t growth_interval);
 int orc_step_decision(const double* rank_sqnorms, const int32_t* rank_flags, int32_t n_ranks, double max_norm,
@@ -83,6 +97,13 @@ int orc_step_decision(const double* rank_sqnorms, const int32_t* rank_flags, int
                       int32_t* skip, double* global_norm);
 double orc_cosine_lr(int64_t t, int64_t total, double lr_max, double lr_min);
 
+/* AdamW on the shard (reading: torch.optim.AdamW convention; the pages name
+ * AdamW but print no equations).  Pinned to: torch.optim.AdamW in fp64 and
+ * fp32, the fp64 variant within its rounding bound, the step-1 closed form,
+ * a four-element two-step worked example, lr = 0 / beta = 0 / zero padding
+ * special cases, the shard-concatenation invariance; fp16 parameters to
+ * torch's binary16 conversion.  The update form itself is a reading (parity
+ * unpinned by the pages). */
 int orc_adamw_scalars(const orc_hparams* hp, orc_scalars* out);
 int orc_adamw_step(const uint16_t* grad, int32_t dtype, float* master, float* m, float* v,
                    uint16_t* param16, int32_t param_dtype, int64_t n, const orc_hparams* hp);
@@ -92,7 +113,9 @@ int orc_adamw_step(const uint16_t* grad, int32_t dtype, float* master, float* m,
 int orc_adamw_step_f64(const double* grad, double* master, double* m, double* v, int64_t n,
                        const orc_hparams* hp);
 
-/* Number codecs. */
+/* Number codecs.  Pinned to: all 65536 patterns of each 16-bit format
+ * against torch / numpy; rounding to bf16 and to binary16 against torch and
+ * numpy on every rounding boundary and millions of random patterns. */
 float orc_bf16_to_f32(uint16_t h);
 float orc_f16_to_f32(uint16_t h);
 uint16_t orc_f32_to_bf16(float f);
