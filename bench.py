@@ -51,6 +51,10 @@ def parse():
     ap.add_argument("--produce", action="store_true",
                     help="produce the rank's gradients inside every timed step (the synthetic generator stands in "
                          "for backward): before the step, or bucket by bucket on a producer stream with --bucket")
+    ap.add_argument("--source-sets", type=int, default=2,
+                    help="identical copies of the source gradients, used in turn by successive steps, so that a "
+                         "step's gradients come from HBM rather than from the Infinity Cache left by the last step "
+                         "(one-pass paths; the bucketed path uses one)")
     ap.add_argument("--producer", choices=("separate", "same"), default="separate",
                     help="with --produce: generate gradients on their own stream (default) or on the compute stream")
     ap.add_argument("--event-every", type=int, default=4,
@@ -184,6 +188,14 @@ def main():
     if flat:
         sh.grad[lay.shard_valid:].zero_()
         synth.fill_tensor(gf, lay.shard_offset, sh.grad[:lay.shard_valid])
+    # Further copies of the sources (same values) with their own flatten tables, used in turn.
+    n_sets = 1 if (flat or args.bucket) else max(1, args.source_sets)
+    source_sets, tables = [sources], [sh.seg_table]
+    for _ in range(1, n_sets):
+        copy = [x.clone() if x is not None else None for x in sources]
+        blob = Z.zero_flatten_plan(sh.segments, [x if x is not None else 0 for x in copy])
+        source_sets.append(copy)
+        tables.append(torch.frombuffer(bytearray(blob), dtype=torch.uint8).to(dev))
     master0 = torch.zeros(lay.shard_numel, dtype=torch.float32, device=dev)
     synth.fill_tensor(w.master_field(), lay.shard_offset, master0[:lay.shard_valid])
     sh.load_master(master0)
@@ -201,11 +213,14 @@ def main():
         prod_stream = torch.cuda.Stream() if args.producer == "separate" else torch.cuda.current_stream()
     landing_set = set(landing)
 
+    current = [0]  # the source set the step in flight uses
+
     def produce(idx, st):
         """Writes the gradients of source tensors `idx` (those that land in the shard) on stream `st`."""
+        srcs = source_sets[current[0]]
         for t in idx:
             if t in landing_set:
-                synth.fill_device(gf, starts[t], w.numels[t], sources[t].data_ptr(), st.cuda_stream)
+                synth.fill_device(gf, starts[t], w.numels[t], srcs[t].data_ptr(), st.cuda_stream)
 
     pipe = None
     if args.bucket:
@@ -236,6 +251,8 @@ def main():
                                    ctypes.byref(lay_out), ctypes.cast(seg_buf, ctypes.c_void_p), len(segs),
                                    ctypes.byref(nseg))
         assert rc == 0 and nseg.value == len(segs)
+        current[0] = (current[0] + 1) % n_sets
+        sh.seg_table = tables[current[0]]
         if pipe is not None:                           # fixed-capacity buckets, last bucket first
             if args.produce:                           # backward stand-in on the producer stream
                 pipe.launch_production(produce, prod_stream, stream)
@@ -373,6 +390,7 @@ def main():
             "decision": args.decision,
             "bucket_numel": args.bucket or None,
             "gradients_produced_in_step": args.produce,
+            "source_sets": n_sets,
             "producer_stream": args.producer if args.produce else None,
             "buckets": len(pipe.windows) if pipe is not None else None,
             "flatten_norm_fused": sh.fused,
