@@ -130,7 +130,8 @@ def test_config_parity(name):
             hb = int(bits.view(np.uint16)[0]) if gdt == Z.ZERO_FP16 else int(bits.view(np.uint32)[0] >> 16)
             inject_at = (j, hb)
             sg = next(x for x in segs if x.dst_offset <= j < x.dst_offset + x.numel)
-            sources[sg.tensor].view(torch.int16)[sg.src_offset + j - sg.dst_offset] = hb - (1 << 16 if hb >= 1 << 15 else 0)
+            signed = hb - (1 << 16 if hb >= 1 << 15 else 0)  # the same 16 bits as a signed int16
+            sources[sg.tensor].view(torch.int16)[sg.src_offset + j - sg.dst_offset] = signed
         if w.lr_min is not None:
             cfg.lr = Z.zero_cosine_lr(t, w.steps, w.lr, w.lr_min)
             olr = oracle.cosine_lr(t, w.steps, w.lr, w.lr_min)

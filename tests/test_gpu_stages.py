@@ -95,3 +95,60 @@ def test_zero1_zero2_and_dp_agree():
         q = torch.cat([sh.param for sh in z2])
         if same:
             assert torch.equal(q.view(torch.int16), dp.param.view(torch.int16))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_eight_ranks_equal_dp_at_gpt2_scale():
+    """All eight rank shards of the GPT-2 1.5B configuration (1,557,611,200 parameters, 47+ tensor pieces per
+    rank), each flattened from the per-tensor gradients, normed, decided and updated on the GPU, then laid end
+    to end, against one unsharded rank over the whole model: equal bit for bit whenever the two fp32 factors
+    coincide (several fp64 summation orders are correct)."""
+    from synth.workloads import WORKLOADS
+
+    w = WORKLOADS["gpt2-1.5b"]
+    psi, world = sum(w.numels), w.world
+    cfg = AdamWConfig(lr=3e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, max_norm=1.0)
+    offs = np.cumsum([0] + list(w.numels))
+    srcs = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for n in w.numels]
+    zs = [RankShard(w.numels, world, r, Z.ZERO_BF16, DEV, sources=srcs, tiled=True, fused=True) for r in range(world)]
+    s = zs[0].n
+    assert world * s == psi  # 8 | Ψ here: no padding, so the shards tile the model exactly
+    master = torch.empty(psi, device=DEV)
+    synth.fill_tensor(synth.field(SEED, synth.STREAM_MASTER, 0, 0.02, synth.F32), 0, master)
+    for r, sh in enumerate(zs):
+        sh.load_master(master[r * s:(r + 1) * s].contiguous())
+    dz = DeviceDecision(zs, cfg)
+    flat = torch.empty(psi, dtype=torch.bfloat16, device=DEV)
+    dp = RankShard([psi], 1, 0, Z.ZERO_BF16, DEV, tiled=True)
+    dp.grad = flat
+    dp.load_master(master)
+    del master
+    ddp = DeviceDecision([dp], cfg)
+    compared = 0
+    for t in range(1, 4):
+        print(f"[gpt2 x8 vs DP] step {t}", flush=True)
+        f = _field(t)
+        for k, src in enumerate(srcs):
+            synth.fill_tensor(f, int(offs[k]), src)
+        synth.fill_tensor(f, 0, flat)
+        dz.step()
+        ddp.step(flatten=False)
+        torch.cuda.synchronize()
+        sz, sdp = dz.read(), ddp.read()
+        assert sz["skip"] == sdp["skip"] == 0 and sz["adam_step"] == sdp["adam_step"] == t
+        same = assert_grad_scale_close(sdp["grad_scale"], sz["grad_scale"], psi, f"step {t}")
+        for r, sh in enumerate(zs):  # the gradient shards are the model's gradients, in order
+            assert torch.equal(sh.grad.view(torch.int16), flat[r * s:(r + 1) * s].view(torch.int16)), (t, r)
+        if same:
+            compared += 1
+            dpm = dp.read_state()  # untiled master / m / v of the whole model
+            for r, sh in enumerate(zs):
+                zm = sh.read_state()
+                lo, hi = r * s, (r + 1) * s
+                for k in range(3):
+                    assert torch.equal(zm[k].view(torch.int32), dpm[k][lo:hi].view(torch.int32)), (t, r, k)
+                assert torch.equal(sh.param.view(torch.int16), dp.param[lo:hi].view(torch.int16)), (t, r)
+                del zm
+            del dpm
+    assert compared >= 1  # the factors coincide except with probability ~1e-4 per step
