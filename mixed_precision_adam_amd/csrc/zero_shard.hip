@@ -241,7 +241,8 @@ constexpr int kAdamUnroll = 1;
 // Tiled optimizer state (ZERO_STATE_TILE = 1024 elements per tile): tile k
 // stores master, m and v of elements [1024k, 1024k+1024) back to back, so the
 // update streams three address ranges (grad, state, param) instead of five.
-// One 256-thread workgroup per tile (tile0 + blockIdx.x); thread t owns the
+// One 256-thread workgroup per tile (tile0 + an XCD-grouped blockIdx.x, see
+// xcd_grouped); thread t owns the
 // group of four elements 4t .. 4t+3 (kTileUnits groups in general, issuing
 // every load before any arithmetic).  Measured on MI355X, one group per thread and 12 KiB of state
 // per workgroup beats two groups / 24 KiB by 4%, provided every store carries
@@ -250,6 +251,22 @@ constexpr int kAdamUnroll = 1;
 // element (the tile's padding floats keep their bits).
 constexpr int64_t kTile = ZERO_STATE_TILE;
 constexpr int kTileUnits = 1;
+
+// The dispatcher deals a launch's workgroups to the eight XCDs in turn, so
+// workgroup b runs on XCD b mod 8.  Remapping workgroups to tiles so that each
+// XCD takes kXcdGroup adjacent tiles at a time (the first 8·kXcdGroup
+// workgroups cover 8·kXcdGroup adjacent tiles, XCD x taking the x-th run of
+// kXcdGroup) measured 0.5-1.2% faster on MI355X boxes for groups of 8 to 16
+// tiles, against no grouping; a whole contiguous range per XCD was 2-3%
+// slower.  A bijection on [0, n): workgroups past the last whole span of
+// 8·kXcdGroup keep their own index.
+constexpr int64_t kXcds = 8, kXcdGroup = 8;
+__device__ __forceinline__ int64_t xcd_grouped(int64_t b, int64_t n) {
+  constexpr int64_t kSpan = kXcds * kXcdGroup;
+  if (b >= n / kSpan * kSpan) return b;
+  const int64_t x = b % kXcds, q = b / kXcds;
+  return q / kXcdGroup * kSpan + x * kXcdGroup + q % kXcdGroup;
+}
 constexpr int64_t kTile4 = kTile / 4;  // 16-byte vectors per array per tile
 static_assert(kTile4 == kBlock * kTileUnits, "each thread owns kTileUnits groups of 4 elements of a tile");
 
@@ -259,7 +276,7 @@ __global__ __launch_bounds__(kBlock) void adamw_tiled_kernel(const uint16_t* __r
                                                              uint16_t* __restrict__ param16, int64_t n,
                                                              int64_t tile0, AdamScalars s,
                                                              const zero_step_state* dev) {
-  const int64_t tile = tile0 + blockIdx.x;
+  const int64_t tile = tile0 + xcd_grouped(blockIdx.x, gridDim.x);
   f32x4* base = state + tile * (3 * kTile4);
   u32x2 g[kTileUnits];
   f32x4 p[kTileUnits], m[kTileUnits], v[kTileUnits];
