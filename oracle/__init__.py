@@ -19,7 +19,9 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+# A test that plants mistakes in a copy of the oracle points this at the mutated build.
+_LIB_PATH = os.environ.get("ZERO_ORACLE_LIB") or _DEFAULT_LIB
 
 BF16 = 0
 FP16 = 1
@@ -84,6 +86,8 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB_PATH):
+        if _LIB_PATH != _DEFAULT_LIB:
+            raise FileNotFoundError(_LIB_PATH)
         build()
     lib = C.CDLL(_LIB_PATH)
     P = C.c_void_p
