@@ -214,13 +214,23 @@ def main():
     landing_set = set(landing)
 
     current = [0]  # the source set the step in flight uses
+    piece_tables = {}  # (source set, tensors) -> device piece table, built once (in the warm-up steps)
 
     def produce(idx, st):
-        """Writes the gradients of source tensors `idx` (those that land in the shard) on stream `st`."""
-        srcs = source_sets[current[0]]
-        for t in idx:
-            if t in landing_set:
-                synth.fill_device(gf, starts[t], w.numels[t], srcs[t].data_ptr(), st.cuda_stream)
+        """Writes the gradients of source tensors `idx` (those that land in the shard) on stream `st`: one
+        generator launch for all of them."""
+        key = (current[0], tuple(t for t in idx if t in landing_set))
+        if not key[1]:
+            return
+        if key not in piece_tables:
+            srcs = source_sets[current[0]]
+            pieces = [(srcs[t].data_ptr(), starts[t], w.numels[t]) for t in key[1]]
+            blob = synth.piece_table(pieces)
+            piece_tables[key] = (torch.frombuffer(bytearray(blob), dtype=torch.uint8).to(dev), len(pieces),
+                                 max(w.numels[t] for t in key[1]))
+            torch.cuda.synchronize()  # the table is in place before any stream reads it
+        table, n_pieces, max_n = piece_tables[key]
+        synth.fill_device_many(gf, table.data_ptr(), n_pieces, max_n, st.cuda_stream)
 
     pipe = None
     if args.bucket:

@@ -61,6 +61,7 @@ def _load():
         lib = C.CDLL(_LIB_PATH)
         lib.syn_fill_host.argtypes = [C.POINTER(Field), C.c_int64, C.c_int64, C.c_void_p, C.c_int32]
         lib.syn_fill_device.argtypes = [C.POINTER(Field), C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
+        lib.syn_fill_device_many.argtypes = [C.POINTER(Field), C.c_void_p, C.c_int32, C.c_int64, C.c_void_p]
         _lib = lib
     return _lib
 
@@ -88,6 +89,24 @@ def fill_device(f: Field, idx0: int, n: int, ptr: int, stream: int) -> None:
     rc = _load().syn_fill_device(C.byref(f), idx0, n, ptr, stream)
     if rc != 0:
         raise RuntimeError(f"syn_fill_device failed ({rc})")
+
+
+class Piece(C.Structure):
+    _fields_ = [("out", C.c_void_p), ("idx0", C.c_int64), ("n", C.c_int64)]
+
+
+def piece_table(pieces) -> bytes:
+    """Packs (device address, first flat index, element count) triples for fill_device_many; the caller
+    copies the bytes to device memory once and reuses them."""
+    arr = (Piece * max(len(pieces), 1))(*[Piece(p, i, n) for p, i, n in pieces])
+    return bytes(arr)[:len(pieces) * C.sizeof(Piece)]
+
+
+def fill_device_many(f: Field, table_dev: int, n_pieces: int, max_n: int, stream: int) -> None:
+    """Every piece of a device-resident piece table written in one launch on HIP stream `stream`."""
+    rc = _load().syn_fill_device_many(C.byref(f), table_dev, n_pieces, max_n, stream)
+    if rc != 0:
+        raise RuntimeError(f"syn_fill_device_many failed ({rc})")
 
 
 def fill_tensor(f: Field, idx0: int, t) -> None:

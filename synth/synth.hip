@@ -38,6 +38,16 @@ __global__ void fill_kernel(syn_field f, uint64_t key, uint64_t okey, int64_t id
 
 bool field_ok(const syn_field* f) { return f && f->kind <= SYN_FP16 && f->outlier_per_million <= 1000000u; }
 
+// One row of workgroups per piece: piece p = blockIdx.y writes its elements
+// idx0 .. idx0+n-1 to its own buffer, grid-stride over blockIdx.x.
+__global__ void fill_many_kernel(syn_field f, uint64_t key, uint64_t okey, const syn_piece* pieces) {
+  const syn_piece pc = pieces[blockIdx.y];
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < pc.n; j += stride) {
+    fill_one(f, key, okey, (uint64_t)(pc.idx0 + j), pc.out, j);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,6 +87,21 @@ int syn_fill_device(const syn_field* f, int64_t idx0, int64_t n, void* out_dev, 
   int64_t blocks = std::min<int64_t>((n + 255) / 256, 8192);
   hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, *f, key, okey, idx0, n,
                      out_dev);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// Several buffers in one launch: pieces_dev is a device array of n_pieces
+// syn_piece records (the longest holding max_n elements); each gets exactly
+// what syn_fill_device would write for it.
+int syn_fill_device_many(const syn_field* f, const syn_piece* pieces_dev, int32_t n_pieces, int64_t max_n,
+                         void* stream) {
+  if (!field_ok(f) || n_pieces < 0 || n_pieces > 65535 || max_n < 0 || (n_pieces > 0 && !pieces_dev)) return -1;
+  if (n_pieces == 0 || max_n == 0) return 0;
+  const uint64_t key = syn_key(f->seed, f->stream, f->step);
+  const uint64_t okey = syn_key(f->seed, f->stream + kOutlierStreamOffset, f->step);
+  const int64_t blocks = std::min<int64_t>((max_n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_many_kernel, dim3((unsigned)blocks, (unsigned)n_pieces), dim3(256), 0, (hipStream_t)stream,
+                     *f, key, okey, pieces_dev);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -43,6 +43,14 @@ typedef struct {
 
 enum { SYN_F32 = 0, SYN_BF16 = 1, SYN_FP16 = 2 };
 
+/* One destination of a multi-buffer device fill: elements idx0 .. idx0+n-1
+ * of the field, written to out[0 .. n). */
+typedef struct {
+  void* out;
+  int64_t idx0;
+  int64_t n;
+} syn_piece;
+
 SYN_HD uint64_t syn_mix64(uint64_t z) {
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
