@@ -261,11 +261,14 @@ constexpr int kTileUnits = 1;
 // workgroup b runs on XCD b mod 8.  Remapping workgroups to tiles so that each
 // XCD takes kXcdGroup adjacent tiles at a time (the first 8·kXcdGroup
 // workgroups cover 8·kXcdGroup adjacent tiles, XCD x taking the x-th run of
-// kXcdGroup) measured 0.5-1.2% faster on MI355X boxes for groups of 8 to 16
-// tiles, against no grouping; a whole contiguous range per XCD was 2-3%
-// slower.  A bijection on [0, n): workgroups past the last whole span of
-// 8·kXcdGroup keep their own index.
-constexpr int64_t kXcds = 8, kXcdGroup = 8;
+// kXcdGroup) is faster on MI355X: groups of 8 gained 0.5-1.2% over no
+// grouping, and with the occupancy cap below, update time on the GPT-2 rank
+// shard relative to groups of 8 is: 16 -0.3%, 20 -0.6%, 24 -1.9%, 28 +0.5%,
+// 32 -1.2%, 40 +0.8%, 48 -1.1%, 64 +0.2%; with 24 the Llama-7B, Llama-13B
+// and 1T shards gain 1.7% too.  A whole contiguous range per XCD was 2-3%
+// slower than no grouping.  A bijection on [0, n): workgroups past the last
+// whole span of 8·kXcdGroup keep their own index.
+constexpr int64_t kXcds = 8, kXcdGroup = 24;
 __device__ __forceinline__ int64_t xcd_grouped(int64_t b, int64_t n) {
   constexpr int64_t kSpan = kXcds * kXcdGroup;
   if (b >= n / kSpan * kSpan) return b;

@@ -329,7 +329,10 @@ def _tiled_case(n, dt, gq_offset, hp, steps, seed):
         assert (tail == 0).all()
 
 
-@pytest.mark.parametrize("n", [1, 5, 1023, 1024, 1025, 2047, 2048, 2049, 2048 + 1027, 4096 * 3 + 7, 100_003])
+# 192 * 1024 + 5 and 3 * 192 * 1024 + 1027: just past one and three spans of the XCD tile grouping (8 XCDs x 24
+# tiles), ragged
+@pytest.mark.parametrize("n", [1, 5, 1023, 1024, 1025, 2047, 2048, 2049, 2048 + 1027, 4096 * 3 + 7, 100_003,
+                               192 * 1024 + 5, 3 * 192 * 1024 + 1027])
 @pytest.mark.parametrize("dt", [0, 1])
 def test_adamw_tiled_sizes(n, dt):
     _tiled_case(n, dt, 0, HP_SETS[0], 2, n + 7 * dt)
