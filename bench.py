@@ -57,7 +57,7 @@ def parse():
                          "(one-pass paths; the bucketed path uses one)")
     ap.add_argument("--producer", choices=("separate", "same"), default="separate",
                     help="with --produce: generate gradients on their own stream (default) or on the compute stream")
-    ap.add_argument("--event-every", type=int, default=4,
+    ap.add_argument("--event-every", type=int, default=10,
                     help="bracket the kernels of every k-th timed step with HIP events (each record costs ~3 us)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-sample", type=int, default=0, help="elements of the shard the oracle times (0: all)")
