@@ -392,3 +392,55 @@ def test_tile_untile_roundtrip():
         assert torch.equal(tiles[:, 2, :].reshape(-1)[:n], src[2])
         if n % T:
             assert (tiles[-1][:, n % T:] == 7.0).all()
+
+
+def _same_or_both_nan(got, ref, what):
+    got, ref = np.asarray(got, np.float32), np.asarray(ref, np.float32)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all(), f"{what}: NaN positions differ"
+    bad = np.nonzero(got[~nan].view(np.uint32) != ref[~nan].view(np.uint32))[0]
+    assert bad.size == 0, f"{what}: {bad.size} elements differ, e.g. got {got[~nan][bad[:4]]} want {ref[~nan][bad[:4]]}"
+
+
+@pytest.mark.parametrize("layout", ["arrays", "tiled"])
+@pytest.mark.parametrize("gscale", [1.0, 2.0**-16, 65536.0])
+def test_adamw_extreme_values(layout, gscale):
+    """Gradients at the edges of bf16 (largest finite, smallest normal, subnormals, signed zeros) and masters at
+    the edges of fp32 (largest finite, subnormals, signed zeros), scaled so that products overflow, quotients
+    reach inf/inf and results go subnormal: every element must come out bit for bit as the oracle's (both
+    evaluate the same correctly rounded IEEE operations with subnormals kept), NaN where the oracle has NaN."""
+    g_pat = np.array([0x7F7F, 0xFF7F, 0x0080, 0x8080, 0x0001, 0x8001, 0x007F, 0x0000, 0x8000, 0x3F80, 0xBF80,
+                      0x3DCD, 0x7F00, 0x00FF], dtype=np.uint16)
+    m_pat = np.array([3.4028235e38, -3.4028235e38, 1e-45, -1e-45, 1.1754944e-38, 0.0, -0.0, 1.0, -2.0, 1e30,
+                      1e-30, 5.877472e-39, 65504.0, -7.0e-39], dtype=np.float32)
+    rng = np.random.default_rng(int(gscale * 1000) % 2**31 + (layout == "tiled"))
+    n = 4096 + 37
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)
+    p0 = m_pat[rng.integers(0, m_pat.size, n)]
+    p = torch.from_numpy(p0.copy()).to(DEV)
+    m, v = torch.zeros(n, device=DEV), torch.zeros(n, device=DEV)
+    q = torch.zeros(n, dtype=torch.bfloat16, device=DEV)
+    if layout == "tiled":
+        state = torch.zeros(Z.zero_state_tiled_numel(n), device=DEV)
+        Z.zero_state_tile(p, m, v, state, n)
+    rp, rm, rv, rq = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32), np.zeros(n, np.uint16)
+    for t in range(1, 4):
+        gb = g_pat[rng.integers(0, g_pat.size, n)]
+        g = to_dev16(gb, torch.bfloat16)
+        if layout == "tiled":
+            Z.zero_adamw_step_tiled(g, 0, state, q, n, grad_scale=gscale, step=t, **hp)
+            out = [torch.empty(n, device=DEV) for _ in range(3)]
+            Z.zero_state_untile(state, *out, n)
+        else:
+            Z.zero_adamw_step(g, 0, p, m, v, q, n, grad_scale=gscale, step=t, **hp)
+            out = [p, m, v]
+        oracle.adamw_step(gb, 0, rp, rm, rv, rq, grad_scale=gscale, step=t, **hp)
+        torch.cuda.synchronize()
+        what = f"extreme {layout} gscale={gscale} t={t}"
+        for k, (x, r) in enumerate(zip(out, (rp, rm, rv))):
+            _same_or_both_nan(x.cpu().numpy(), r, f"{what} {('master', 'm', 'v')[k]}")
+        qg = bits16(q)
+        nanq = (rq & 0x7F80) == 0x7F80
+        nanq &= (rq & 0x7F) != 0
+        assert (qg[~nanq] == rq[~nanq]).all(), what
+        assert (((qg[nanq] & 0x7F80) == 0x7F80) & ((qg[nanq] & 0x7F) != 0)).all(), what
