@@ -206,10 +206,9 @@ def main():
     scaler = ScalerState(scale=w.loss_scale, growth_interval=growth)
     ddec = DeviceDecision([sh], cfg, loss_scale=w.loss_scale, growth_interval=growth) if args.decision == "device" \
         else None
-    if args.produce:
-        assert args.decision == "device", "--produce needs the device decision"
     prod_stream = None
     if args.produce:
+        assert args.decision == "device", "--produce needs the device decision"
         prod_stream = torch.cuda.Stream() if args.producer == "separate" else torch.cuda.current_stream()
     landing_set = set(landing)
 
