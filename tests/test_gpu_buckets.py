@@ -96,3 +96,45 @@ def test_sqnorm_reduce_exact_on_integers_and_flags():
                 flags[at] = 7
                 Z.zero_sqnorm_reduce(ps, torch.from_numpy(flags).to(DEV), count, sq, fl)
                 assert out.cpu().numpy()[1:].view(np.int32)[0] == 1, (count, at)
+
+
+def test_bucket_pipeline_fp16_overflow_skips_and_halves():
+    """fp16 gradients under a dynamic loss scale, in buckets: a +inf in one bucket sets that bucket's partial
+    flag, the fold carries it to the decision, the step is skipped (state untouched, Adam t unchanged) and the
+    scale halves; the next step proceeds."""
+    numels = gpt2_tensors(d=128, layers=2, vocab=1000, ctx=64, ffn=512)[1]
+    starts = np.cumsum([0] + numels)
+    srcs = [torch.empty(n, dtype=torch.float16, device=DEV) for n in numels]
+    sh = RankShard(numels, 2, 1, Z.ZERO_FP16, DEV, sources=srcs, tiled=True, fused=True)
+    lay = sh.layout
+    p0 = torch.zeros(sh.n, device=DEV)
+    synth.fill_tensor(synth.field(SEED, synth.STREAM_MASTER, 0, 0.02, synth.F32), lay.shard_offset,
+                      p0[:lay.shard_valid])
+    sh.load_master(p0)
+    cfg = AdamWConfig(lr=1e-3, max_norm=1.0)
+    pipe = BucketPipeline(sh, srcs, 8192, cfg, loss_scale=1024.0, growth_interval=1000)
+    assert len(pipe.windows) > 3
+
+    def fill(t, scale, inf_at=None):
+        f = synth.field(SEED, synth.STREAM_GRAD, t, 1e-3, synth.FP16, scale=scale)
+        for k, src in enumerate(srcs):
+            synth.fill_tensor(f, int(starts[k]), src)
+        if inf_at is not None:  # a shard element in the middle of one bucket
+            sg = next(x for x in sh.segments if x.dst_offset <= inf_at < x.dst_offset + x.numel)
+            srcs[sg.tensor].view(torch.int16)[sg.src_offset + inf_at - sg.dst_offset] = 0x7C00
+
+    fill(1, 1024.0)
+    pipe.step()
+    s1 = pipe.read()
+    assert s1["skip"] == 0 and s1["adam_step"] == 1 and s1["loss_scale"] == 1024.0
+    before = sh.state.clone(), sh.param.clone()
+    fill(2, 1024.0, inf_at=2 * 8192 + 77)
+    pipe.step()
+    s2 = pipe.read()
+    assert s2["skip"] == 1 and s2["adam_step"] == 1 and s2["loss_scale"] == 512.0 and s2["iteration"] == 2
+    assert torch.equal(sh.state.view(torch.int32), before[0].view(torch.int32))
+    assert torch.equal(sh.param.view(torch.int16), before[1].view(torch.int16))
+    fill(3, 512.0)
+    pipe.step()
+    s3 = pipe.read()
+    assert s3["skip"] == 0 and s3["adam_step"] == 2 and s3["loss_scale"] == 512.0
