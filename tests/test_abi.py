@@ -219,3 +219,31 @@ def test_flatten_partials_count_is_not_monotone():
     lib = Z.library()
     assert lib.zero_sqnorm_reduce(None, None, 4, 16, 16, None) == Z.ZERO_ERR_INVALID
     assert lib.zero_flatten_grads_partials(16, 1, 0, 16, 8, None, None, None) == Z.ZERO_ERR_INVALID
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/zero_shard.h compiles as strict C99 and C11 (-pedantic, warnings as errors), and a C program
+    built against it links to the library and calls a host entry point (capacity query of the layout)."""
+    import shutil
+    import subprocess
+
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use.c"
+    src.write_text('#include "zero_shard.h"\n'
+                   "int main(void) {\n"
+                   "  zero_layout lay;\n"
+                   "  int32_t n = 0;\n"
+                   "  int64_t numels[2] = {10, 7};\n"
+                   "  int rc = zero_shard_layout(numels, 2, 4, 3, &lay, 0, 0, &n);\n"
+                   "  return (rc == ZERO_ERR_CAPACITY && n == 1 && lay.shard_numel == 5) ? 0 : 1;\n"
+                   "}\n")
+    inc = os.path.join(os.path.dirname(HEADER))
+    for std in ("c99", "c11"):
+        subprocess.run(["gcc", f"-std={std}", "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only", "-I", inc,
+                        str(src)], check=True)
+    exe = str(tmp_path / "use")
+    libdir = os.path.dirname(Z.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-I", inc, "-o", exe, str(src), "-L", libdir, "-l:libzero_shard.so",
+                    f"-Wl,-rpath,{libdir}"], check=True)
+    assert subprocess.run([exe]).returncode == 0
