@@ -339,7 +339,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        dec = step(pool[k] if k % args.event_every == args.event_every - 1 or args.steps < args.event_every else None)
+        sample = k % args.event_every == args.event_every - 1 or (args.steps < args.event_every and k == args.steps - 1)
+        dec = step(pool[k] if sample else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
