@@ -294,7 +294,9 @@ int64_t zero_state_tiled_numel(int64_t n);
 int zero_adamw_step_tiled(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev,
                           zero_dtype pdt, int64_t n, const zero_adamw_hparams* hp, void* stream);
 /* Device bit copies between separate master/m/v arrays and the tiled state
- * (for initialisation and checkpoints); padding floats are left untouched. */
+ * (for initialisation and checkpoints); padding floats are left untouched.
+ * All four buffers must be 4-byte aligned; NULL buffers (n > 0), n outside
+ * [0, ZERO_MAX_NUMEL] or misalignment give ZERO_ERR_INVALID. */
 int zero_state_tile(const float* master_dev, const float* m_dev, const float* v_dev, float* state_dev, int64_t n,
                     void* stream);
 int zero_state_untile(const float* state_dev, float* master_dev, float* m_dev, float* v_dev, int64_t n, void* stream);

@@ -62,6 +62,10 @@ constexpr int kBlock = 256;  // 4 wavefronts of 64
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+inline bool fp32_aligned(const void* a, const void* b, const void* c, const void* d) {
+  return ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) | reinterpret_cast<uintptr_t>(c) |
+           reinterpret_cast<uintptr_t>(d)) & 3u) == 0;
+}
 
 // ------------------------------------------------------------------ 16-bit formats
 
@@ -749,8 +753,7 @@ int launch_adamw_arrays(const char* fn, const void* grad_dev, int gdt, float* ma
                         uint16_t* param_dev, int pdt, int64_t n, const AdamScalars& s, const zero_step_state* dev,
                         hipStream_t st) {
   if (n > 0 && (!master_dev || !m_dev || !v_dev)) return fail(ZERO_ERR_INVALID, "%s: NULL state", fn);
-  if (((reinterpret_cast<uintptr_t>(master_dev) | reinterpret_cast<uintptr_t>(m_dev) |
-        reinterpret_cast<uintptr_t>(v_dev)) & 3u) != 0)
+  if (!fp32_aligned(master_dev, m_dev, v_dev, nullptr))
     return fail(ZERO_ERR_INVALID, "%s: fp32 buffers not 4-byte aligned", fn);
   if (n == 0) return ZERO_OK;
   const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
@@ -1248,7 +1251,8 @@ int zero_step_decision_dev(const double* rank_sqnorms_dev, const int32_t* rank_f
 
 int zero_state_tile(const float* master_dev, const float* m_dev, const float* v_dev, float* state_dev, int64_t n,
                     void* stream) {
-  if (n < 0 || n > kMaxPsi || (n > 0 && (!master_dev || !m_dev || !v_dev || !state_dev)))
+  if (n < 0 || n > kMaxPsi || (n > 0 && (!master_dev || !m_dev || !v_dev || !state_dev)) ||
+      !fp32_aligned(master_dev, m_dev, v_dev, state_dev))
     return fail(ZERO_ERR_INVALID, "zero_state_tile: bad arguments");
   if (n == 0) return ZERO_OK;
   const int64_t blocks = std::min<int64_t>(ceil_div(n, kBlock), 65536);
@@ -1259,7 +1263,8 @@ int zero_state_tile(const float* master_dev, const float* m_dev, const float* v_
 }
 
 int zero_state_untile(const float* state_dev, float* master_dev, float* m_dev, float* v_dev, int64_t n, void* stream) {
-  if (n < 0 || n > kMaxPsi || (n > 0 && (!master_dev || !m_dev || !v_dev || !state_dev)))
+  if (n < 0 || n > kMaxPsi || (n > 0 && (!master_dev || !m_dev || !v_dev || !state_dev)) ||
+      !fp32_aligned(master_dev, m_dev, v_dev, state_dev))
     return fail(ZERO_ERR_INVALID, "zero_state_untile: bad arguments");
   if (n == 0) return ZERO_OK;
   const int64_t blocks = std::min<int64_t>(ceil_div(n, kBlock), 65536);

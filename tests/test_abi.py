@@ -170,6 +170,8 @@ def test_tiled_numel_and_invalid_tiled_args():
     assert lib.zero_adamw_step_tiled(17, 0, 16, 16, 0, 8, hp, None) == Z.ZERO_ERR_INVALID
     assert lib.zero_state_tile(None, 16, 16, 16, 5, None) == Z.ZERO_ERR_INVALID
     assert lib.zero_state_untile(16, 16, 16, 16, -1, None) == Z.ZERO_ERR_INVALID
+    assert lib.zero_state_tile(16, 16, 16, 18, 5, None) == Z.ZERO_ERR_INVALID  # state not 4-B aligned
+    assert lib.zero_state_untile(16, 16, 22, 16, 5, None) == Z.ZERO_ERR_INVALID  # m not 4-B aligned
     ws = Z.zero_grad_sqnorm_workspace_bytes(100)
     assert lib.zero_flatten_grads_sqnorm(16, 1, 0, 16, 100, 256, ws - 1, 16, 16, None) == Z.ZERO_ERR_INVALID
     assert lib.zero_flatten_grads_sqnorm(12, 1, 0, 16, 100, 256, ws, 16, 16, None) == Z.ZERO_ERR_INVALID
