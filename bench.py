@@ -68,16 +68,25 @@ def parse():
 
 
 def copy_calibration(nbytes: int, reps: int = 10) -> None:
+    """Plain device-to-device copies of nbytes: the reference for the HBM counters' scale and the copy rate
+    the streaming kernels are compared with (read + write bytes per second, timed with HIP events on torch's
+    stream, which the copies run on)."""
     import torch
 
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a.fill_(1)
+    b.copy_(a)  # warm-up
     torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
     for _ in range(reps):
         b.copy_(a)
+    t1.record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+    sec = t0.elapsed_time(t1) * 1e-3 / reps
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps, "ms_per_copy": sec * 1e3,
+                      "copy_gbs": 2 * nbytes / sec / 1e9}))
 
 
 def measured_traffic(kernel: str, workload: str):
