@@ -68,25 +68,40 @@ def parse():
 
 
 def copy_calibration(nbytes: int, reps: int = 10) -> None:
-    """Plain device-to-device copies of nbytes: the reference for the HBM counters' scale and the copy rate
+    """Plain device-to-device copies of nbytes: the reference for the HBM counters' scale, and two copy rates
     the streaming kernels are compared with (read + write bytes per second, timed with HIP events on torch's
-    stream, which the copies run on)."""
+    stream, which every copy here runs on): torch's copy_ (the runtime's copy kernel), and the library's
+    flatten over a single contiguous tensor, which is a plain 16-byte-vector copy kernel."""
     import torch
+
+    import mixed_precision_adam_amd as Z
 
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     b = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     a.fill_(1)
-    b.copy_(a)  # warm-up
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
-        b.copy_(a)
-    t1.record()
-    torch.cuda.synchronize()
-    sec = t0.elapsed_time(t1) * 1e-3 / reps
+    n = nbytes // 2  # 16-bit elements
+    _, segs = Z.zero_shard_layout([n], 1, 0)
+    table = torch.frombuffer(bytearray(Z.zero_flatten_plan(segs, [a.data_ptr()])), dtype=torch.uint8).to("cuda")
+
+    def timed(copy) -> float:
+        copy()  # warm-up
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            copy()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e-3 / reps
+
+    sec = timed(lambda: b.copy_(a))
+    b.zero_()  # so that the check below sees what the flatten wrote
+    sec_fl = timed(lambda: Z.zero_flatten_grads(table, len(segs), Z.ZERO_BF16, b, n))
+    if not torch.equal(a, b):
+        raise RuntimeError("flatten copy mismatch")
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps, "ms_per_copy": sec * 1e3,
-                      "copy_gbs": 2 * nbytes / sec / 1e9}))
+                      "copy_gbs": 2 * nbytes / sec / 1e9, "ms_per_flatten_copy": sec_fl * 1e3,
+                      "flatten_copy_gbs": 2 * nbytes / sec_fl / 1e9}))
 
 
 def measured_traffic(kernel: str, workload: str):
