@@ -549,8 +549,10 @@ __global__ __launch_bounds__(kBlock) void sqnorm_fold_chunks_kernel(double* __re
 // 16-byte boundary and the body moves 16-byte vectors.  With ACC the copied
 // values are also squared into acc (fp64) and checked for inf/NaN.  Source
 // reads stream (non-temporal); the shard is stored with ordinary stores: the
-// update reads it back right away, and on MI355X the whole step is 1.4%
-// faster that way (the flatten itself 15%).
+// update reads part of it back from the Infinity Cache right away.  Measured
+// on MI355X against non-temporal stores: the GPT-2 1.5B rank's whole step is
+// 1.2% faster that way (its flatten 3.7%) and the Llama-13B one 0.8-1%,
+// although a plain copy runs 1-2% slower.
 // Source tensors are plain device allocations (global memory); saying so lets
 // the compiler use global rather than flat loads for them.
 typedef const u32x4 __attribute__((address_space(1)))* global_u32x4_ptr;
