@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark: one data-parallel rank's ZeRO step on one MI355X.
 
-A step is the whole hot path on one rank's shard: shard layout (host),
-flatten of the per-tensor bf16 gradients into the rank's contiguous shard,
-fp64 gradient square-norm with the non-finite flag, the host decision (clip
-coefficient, loss scale, skip) after reading the 12-byte result, and the fused
-AdamW update of the fp32 master/m/v shard with the bf16 parameter writeback.
+A step is the whole hot path on one rank's shard: shard layout (host, once),
+flatten of the per-tensor bf16 gradients into the rank's contiguous shard
+fused with the fp64 gradient square-norm and the non-finite flag, the decision
+(clip coefficient, loss scale, skip) on one GPU thread (`--decision host`:
+on the host after a 16-byte readback), and the fused AdamW update of the fp32
+master/m/v shard with the bf16 parameter writeback.  Nothing in a default
+step waits on the host.
 
 Default workload: GPT-2 1.5B tensor list (48 layers, d=1600, ffn 6400, vocab
 50257, ctx 1024), N = 8 data-parallel ranks, rank 0's shard of 194,701,400
