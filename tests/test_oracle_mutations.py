@@ -39,6 +39,31 @@ MUTATIONS = {
     "binary16 ties away from zero": ("  if (rest > 0.5 || (rest == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;",
                                      "  if (rest >= 0.5) r += 1.0;"),
     "binary16 subnormal exponent": ("  if (E < -14) E = -14;", "  if (E < -15) E = -15;"),
+    "second bias correction from beta1": ("  s->bc2_sqrt = (float)sqrt(bc2);", "  s->bc2_sqrt = (float)sqrt(bc1);"),
+    "eps added before the bias correction": ("    d = d / s.bc2_sqrt;\n    d = d + s.eps;",
+                                             "    d = d + s.eps;\n    d = d / s.bc2_sqrt;"),
+    "decay applied after the Adam term": ("    float p = master[i] * s.decay;\n    p = p - u;",
+                                          "    float p = master[i] - u;\n    p = p * s.decay;"),
+    "first moment decays with beta2": ("    float m_old = s.b1 * m[i];", "    float m_old = s.b2 * m[i];"),
+    "second moment decays with beta1": ("    float v_old = s.b2 * v[i];", "    float v_old = s.b1 * v[i];"),
+    "second moment of g, not g squared": ("    float gg = g * g;", "    float gg = g;"),
+    "clip epsilon dropped": ("  double coef = max_norm / (norm + 1e-6);", "  double coef = max_norm / norm;"),
+    "clip on the squared norm": ("  double norm = sqrt(global_sqnorm);", "  double norm = global_sqnorm;"),
+    "scale grows one step late": ("    if (*good_steps >= growth_interval) {", "    if (*good_steps > growth_interval) {"),
+    "overflow keeps the good-step count": ("    *scale = *scale * 0.5;\n    *good_steps = 0;",
+                                           "    *scale = *scale * 0.5;"),
+    "norm unscaled by the scale, not its square": ("    double unscaled = total / (scale * scale);",
+                                                   "    double unscaled = total / scale;"),
+    "update factor ignores the loss scale": ("    *grad_scale = coef / scale;", "    *grad_scale = coef;"),
+    "square-norm accumulated in fp32": ("    acc = acc + sq;", "    acc = (float)(acc + sq);"),
+    "binary16 decode subnormal scale": ("    mag = ldexp((double)frac, -24);", "    mag = ldexp((double)frac, -25);"),
+    "binary16 decode exponent bias": ("    mag = ldexp((double)(frac + 1024), e - 25);",
+                                      "    mag = ldexp((double)(frac + 1024), e - 24);"),
+    "bf16 NaN not kept quiet": ("    return (uint16_t)((u >> 16) | 0x0040u);", "    return (uint16_t)(u >> 16);"),
+    "ZeRO-1 ledger without the full gradients": (
+        "  out->bytes_zero1 = 2 * out->padded_numel + 2 * out->padded_numel + 12 * shard;",
+        "  out->bytes_zero1 = 2 * out->padded_numel + 12 * shard;"),
+    "valid count not clamped to the shard": ("  if (valid > shard) valid = shard;", "  (void)0;"),
 }
 
 
