@@ -63,7 +63,7 @@ def parse():
                     help="bracket the kernels of every k-th timed step with HIP events (each record costs ~3 us)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-sample", type=int, default=0, help="elements of the shard the oracle times (0: all)")
-    ap.add_argument("--cpu-steps", type=int, default=3, help="steps the oracle times")
+    ap.add_argument("--cpu-steps", type=int, default=4, help="steps the oracle times")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run plain device copies of this many bytes (for HBM counter scaling)")
     return ap.parse_args()
