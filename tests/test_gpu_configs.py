@@ -31,24 +31,27 @@ if torch.cuda.is_available():
     import mixed_precision_adam_amd as Z
     from mixed_precision_adam_amd.driver import AdamWConfig, RankShard, ScalerState, rank_norms, rank_update
 
-WIN = 65536
+WIN = 65536        # windows at both ends, around every segment boundary and around update-launch seams
+HASHED = 32        # plus this many chunks of HWIN elements at hashed positions
+HWIN = 1 << 20
 TILE = 1024  # ZERO_STATE_TILE: windows start on tile boundaries
 
 
 def windows(layout, segments):
+    """Sorted, disjoint [a, b) windows of the shard (merged where they touch), each starting on a tile."""
     s = layout.shard_numel
-    starts = {0, max(0, (s - WIN) // TILE * TILE)}
+    spans = [(0, WIN), (max(0, (s - WIN) // TILE * TILE), WIN)]
     for sg in segments[1:]:
-        starts.add(max(0, (sg.dst_offset - WIN // 2) // TILE * TILE))
+        spans.append((max(0, (sg.dst_offset - WIN // 2) // TILE * TILE), WIN))
     launch = 1 << 25  # the update is issued in launches of this many elements: sample their seams
     for k in range(1, min(4, s // launch) + 1):
-        starts.add(max(0, (k * launch - WIN // 2) // TILE * TILE))
-    for k in range(16):
+        spans.append((max(0, (k * launch - WIN // 2) // TILE * TILE), WIN))
+    for k in range(HASHED):
         h = (k * 0x9E3779B97F4A7C15 + 0x632BE59BD9B4E019) % (1 << 64)
-        starts.add((h % max(1, s // TILE)) * TILE)
+        spans.append(((h % max(1, s // TILE)) * TILE, HWIN))
     out = []
-    for a in sorted(starts):
-        b = min(s, a + WIN)
+    for a, n in sorted(spans):
+        b = min(s, a + n)
         if out and a <= out[-1][1]:
             out[-1] = (out[-1][0], max(out[-1][1], b))
         else:
