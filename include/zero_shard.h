@@ -285,7 +285,8 @@ int zero_adamw_step(const void* grad_dev, zero_dtype gdt, float* master_dev, flo
  * ZERO_STATE_TILE elements.  Tile k holds master[T·k .. T·k+T), then m[...],
  * then v[...] (T = ZERO_STATE_TILE, 12·T = 12 KiB per tile), so the update
  * streams three address ranges (grad, state, param) instead of five; on
- * MI355X that is worth 7-20% of achieved bandwidth.  A shard of n
+ * MI355X the tiled update runs about 6% faster than the separate-array one
+ * (6.66 against 6.27 TB/s on a 1.95e8-element shard).  A shard of n
  * elements needs zero_state_tiled_numel(n) floats (the last tile is padded).
  * zero_adamw_step_tiled computes exactly what zero_adamw_step computes (same
  * per-element operations, same bits); state_dev must be 16-byte aligned. */
