@@ -249,3 +249,4 @@ def test_header_is_plain_c_and_links(tmp_path):
     subprocess.run(["gcc", "-std=c11", "-I", inc, "-o", exe, str(src), "-L", libdir, "-l:libzero_shard.so",
                     f"-Wl,-rpath,{libdir}"], check=True)
     assert subprocess.run([exe]).returncode == 0
+
