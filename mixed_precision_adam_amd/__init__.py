@@ -136,11 +136,17 @@ def _check(status: int) -> None:
 
 
 def _addr(x) -> int | None:
-    """Device address of a torch tensor, or an int address as is."""
+    """Device address of a torch tensor, or an int address as is.  Every buffer the entry points take is
+    device memory read as one flat run of elements, so a tensor must be on the GPU and contiguous: a host
+    tensor's address handed to a kernel would fault, and a strided view would be read as if dense."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if not x.is_cuda:
+        raise ValueError(f"a GPU tensor is required, got one on {x.device}")
+    if not x.is_contiguous():
+        raise ValueError(f"a contiguous tensor is required, got strides {tuple(x.stride())}")
     return x.data_ptr()
 
 

@@ -250,3 +250,17 @@ def test_header_is_plain_c_and_links(tmp_path):
                     f"-Wl,-rpath,{libdir}"], check=True)
     assert subprocess.run([exe]).returncode == 0
 
+
+
+def test_host_tensors_are_refused_before_any_call():
+    """A tensor in host memory never reaches a kernel: the binding refuses it before calling the library."""
+    import torch
+
+    x = torch.zeros(64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        Z.zero_grad_sqnorm(x, Z.ZERO_BF16, 64, 256, 4096, 512, 520)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        Z.zero_adamw_step_tiled(16, Z.ZERO_BF16, torch.zeros(3 * 1024), 32, 8, lr=1e-3, beta1=0.9, beta2=0.999,
+                                eps=1e-8, weight_decay=0.0, grad_scale=1.0, step=1)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        Z.zero_flatten_plan(Z.zero_shard_layout([8], 1, 0)[1], [x])
