@@ -150,6 +150,18 @@ def _addr(x) -> int | None:
     return x.data_ptr()
 
 
+def _buf(x, nbytes: int) -> int | None:
+    """_addr(x), after checking that a tensor holds at least the nbytes the entry point will touch (a count
+    larger than the buffer would send a kernel past its end).  Plain int addresses are taken as they are."""
+    if x is not None and not isinstance(x, int) and x.numel() * x.element_size() < nbytes:
+        raise ValueError(f"buffer of {x.numel() * x.element_size()} bytes, the call touches {nbytes}")
+    return _addr(x)
+
+
+_SEG = C.sizeof(zero_flat_seg)
+_STATE = C.sizeof(zero_step_state)
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         import torch
@@ -211,14 +223,19 @@ def zero_flatten_plan(segments, tensor_ptrs) -> bytes:
     """Packs segments + tensor base addresses into the 32-byte device descriptors (returned as bytes)."""
     n = len(segments)
     segs = (zero_segment * max(n, 1))(*segments)
-    ptrs = (C.c_void_p * max(len(tensor_ptrs), 1))(*[_addr(p) for p in tensor_ptrs])
+    need = [0] * len(tensor_ptrs)
+    for sg in segments:  # 16-bit elements [src_offset, src_offset + numel) of each source are read
+        if 0 <= sg.tensor < len(need):
+            need[sg.tensor] = max(need[sg.tensor], 2 * (sg.src_offset + sg.numel))
+    ptrs = (C.c_void_p * max(len(tensor_ptrs), 1))(*[_buf(p, k) for p, k in zip(tensor_ptrs, need)])
     out = (zero_flat_seg * max(n, 1))()
     _check(_lib.zero_flatten_plan(C.cast(segs, _P), n, C.cast(ptrs, _P), len(tensor_ptrs), C.cast(out, _P)))
     return bytes(out)[: n * C.sizeof(zero_flat_seg)]
 
 
 def zero_flatten_grads(segs_dev, n_segs: int, dtype: int, shard, shard_numel: int, stream=None) -> None:
-    _check(_lib.zero_flatten_grads(_addr(segs_dev), n_segs, dtype, _addr(shard), shard_numel, _stream(stream)))
+    _check(_lib.zero_flatten_grads(_buf(segs_dev, _SEG * max(n_segs, 0)), n_segs, dtype,
+                                   _buf(shard, 2 * max(shard_numel, 0)), shard_numel, _stream(stream)))
 
 
 def zero_grad_sqnorm_workspace_bytes(n: int) -> int:
@@ -226,8 +243,8 @@ def zero_grad_sqnorm_workspace_bytes(n: int) -> int:
 
 
 def zero_grad_sqnorm(shard, dtype: int, n: int, ws, ws_bytes: int, sqnorm_out, nonfinite_out, stream=None) -> None:
-    _check(_lib.zero_grad_sqnorm(_addr(shard), dtype, n, _addr(ws), ws_bytes, _addr(sqnorm_out),
-                                 _addr(nonfinite_out), _stream(stream)))
+    _check(_lib.zero_grad_sqnorm(_buf(shard, 2 * max(n, 0)), dtype, n, _buf(ws, ws_bytes), ws_bytes,
+                                 _buf(sqnorm_out, 8), _buf(nonfinite_out, 4), _stream(stream)))
 
 
 def zero_step_decision(rank_sqnorms, rank_flags, max_norm: float, loss_scale: float, good_steps: int,
@@ -260,14 +277,16 @@ def zero_adamw_step(grad, dtype: int, master, m, v, param, n: int, *, lr: float,
                     eps: float, weight_decay: float, grad_scale: float, step: int, stream=None,
                     param_dtype: int = ZERO_BF16) -> None:
     hp = zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, grad_scale, step)
-    _check(_lib.zero_adamw_step(_addr(grad), dtype, _addr(master), _addr(m), _addr(v), _addr(param), param_dtype, n,
-                                C.byref(hp), _stream(stream)))
+    k = max(n, 0)
+    _check(_lib.zero_adamw_step(_buf(grad, 2 * k), dtype, _buf(master, 4 * k), _buf(m, 4 * k), _buf(v, 4 * k),
+                                _buf(param, 2 * k), param_dtype, n, C.byref(hp), _stream(stream)))
 
 
 def zero_flatten_grads_sqnorm(segs_dev, n_segs: int, dtype: int, shard, shard_numel: int, ws, ws_bytes: int,
                               sqnorm_out, nonfinite_out, stream=None) -> None:
-    _check(_lib.zero_flatten_grads_sqnorm(_addr(segs_dev), n_segs, dtype, _addr(shard), shard_numel, _addr(ws),
-                                          ws_bytes, _addr(sqnorm_out), _addr(nonfinite_out), _stream(stream)))
+    _check(_lib.zero_flatten_grads_sqnorm(_buf(segs_dev, _SEG * max(n_segs, 0)), n_segs, dtype,
+                                          _buf(shard, 2 * max(shard_numel, 0)), shard_numel, _buf(ws, ws_bytes),
+                                          ws_bytes, _buf(sqnorm_out, 8), _buf(nonfinite_out, 4), _stream(stream)))
 
 
 def zero_flatten_partials_count(numel: int) -> int:
@@ -276,13 +295,16 @@ def zero_flatten_partials_count(numel: int) -> int:
 
 def zero_flatten_grads_partials(segs_dev, n_segs: int, dtype: int, dst, numel: int, part_sum, part_flag,
                                 stream=None) -> None:
-    _check(_lib.zero_flatten_grads_partials(_addr(segs_dev), n_segs, dtype, _addr(dst), numel, _addr(part_sum),
-                                            _addr(part_flag), _stream(stream)))
+    parts = zero_flatten_partials_count(numel)
+    _check(_lib.zero_flatten_grads_partials(_buf(segs_dev, _SEG * max(n_segs, 0)), n_segs, dtype,
+                                            _buf(dst, 2 * max(numel, 0)), numel, _buf(part_sum, 8 * parts),
+                                            _buf(part_flag, 4 * parts), _stream(stream)))
 
 
 def zero_sqnorm_reduce(part_sum, part_flag, count: int, sqnorm_out, nonfinite_out, stream=None) -> None:
-    _check(_lib.zero_sqnorm_reduce(_addr(part_sum), _addr(part_flag), count, _addr(sqnorm_out), _addr(nonfinite_out),
-                                   _stream(stream)))
+    k = max(count, 0)
+    _check(_lib.zero_sqnorm_reduce(_buf(part_sum, 8 * k), _buf(part_flag, 4 * k), count, _buf(sqnorm_out, 8),
+                                   _buf(nonfinite_out, 4), _stream(stream)))
 
 
 def zero_state_tiled_numel(n: int) -> int:
@@ -293,39 +315,48 @@ def zero_adamw_step_tiled(grad, dtype: int, state, param, n: int, *, lr: float, 
                           eps: float, weight_decay: float, grad_scale: float, step: int, stream=None,
                           param_dtype: int = ZERO_BF16) -> None:
     hp = zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, grad_scale, step)
-    _check(_lib.zero_adamw_step_tiled(_addr(grad), dtype, _addr(state), _addr(param), param_dtype, n, C.byref(hp),
-                                      _stream(stream)))
+    k = max(n, 0)
+    _check(_lib.zero_adamw_step_tiled(_buf(grad, 2 * k), dtype, _buf(state, 4 * zero_state_tiled_numel(k)),
+                                      _buf(param, 2 * k), param_dtype, n, C.byref(hp), _stream(stream)))
 
 
 def zero_state_tile(master, m, v, state, n: int, stream=None) -> None:
-    _check(_lib.zero_state_tile(_addr(master), _addr(m), _addr(v), _addr(state), n, _stream(stream)))
+    k = max(n, 0)
+    _check(_lib.zero_state_tile(_buf(master, 4 * k), _buf(m, 4 * k), _buf(v, 4 * k),
+                                _buf(state, 4 * zero_state_tiled_numel(k)), n, _stream(stream)))
 
 
 def zero_state_untile(state, master, m, v, n: int, stream=None) -> None:
-    _check(_lib.zero_state_untile(_addr(state), _addr(master), _addr(m), _addr(v), n, _stream(stream)))
+    k = max(n, 0)
+    _check(_lib.zero_state_untile(_buf(state, 4 * zero_state_tiled_numel(k)), _buf(master, 4 * k), _buf(m, 4 * k),
+                                  _buf(v, 4 * k), n, _stream(stream)))
 
 
 def zero_step_state_init(state, loss_scale: float, growth_interval: int, stream=None) -> None:
-    _check(_lib.zero_step_state_init(_addr(state), loss_scale, growth_interval, _stream(stream)))
+    _check(_lib.zero_step_state_init(_buf(state, _STATE), loss_scale, growth_interval, _stream(stream)))
 
 
 def zero_step_decision_dev(rank_sqnorms, rank_flags, n_ranks: int, max_norm: float, state, *, lr: float,
                            beta1: float, beta2: float, eps: float, weight_decay: float, stream=None) -> None:
     hp = zero_adamw_hparams(lr, beta1, beta2, eps, weight_decay, 1.0, 1)
-    _check(_lib.zero_step_decision_dev(_addr(rank_sqnorms), _addr(rank_flags), n_ranks, max_norm, C.byref(hp),
-                                       _addr(state), _stream(stream)))
+    k = max(n_ranks, 0)
+    _check(_lib.zero_step_decision_dev(_buf(rank_sqnorms, 8 * k), _buf(rank_flags, 4 * k), n_ranks, max_norm,
+                                       C.byref(hp), _buf(state, _STATE), _stream(stream)))
 
 
 def zero_adamw_step_dev(grad, dtype: int, master, m, v, param, n: int, step_state, stream=None,
                         param_dtype: int = ZERO_BF16) -> None:
-    _check(_lib.zero_adamw_step_dev(_addr(grad), dtype, _addr(master), _addr(m), _addr(v), _addr(param), param_dtype,
-                                    n, _addr(step_state), _stream(stream)))
+    k = max(n, 0)
+    _check(_lib.zero_adamw_step_dev(_buf(grad, 2 * k), dtype, _buf(master, 4 * k), _buf(m, 4 * k), _buf(v, 4 * k),
+                                    _buf(param, 2 * k), param_dtype, n, _buf(step_state, _STATE), _stream(stream)))
 
 
 def zero_adamw_step_tiled_dev(grad, dtype: int, state, param, n: int, step_state, stream=None,
                               param_dtype: int = ZERO_BF16) -> None:
-    _check(_lib.zero_adamw_step_tiled_dev(_addr(grad), dtype, _addr(state), _addr(param), param_dtype, n,
-                                          _addr(step_state), _stream(stream)))
+    k = max(n, 0)
+    _check(_lib.zero_adamw_step_tiled_dev(_buf(grad, 2 * k), dtype, _buf(state, 4 * zero_state_tiled_numel(k)),
+                                          _buf(param, 2 * k), param_dtype, n, _buf(step_state, _STATE),
+                                          _stream(stream)))
 
 
 def read_step_state(state_tensor) -> dict:

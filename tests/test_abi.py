@@ -264,3 +264,18 @@ def test_host_tensors_are_refused_before_any_call():
                                 eps=1e-8, weight_decay=0.0, grad_scale=1.0, step=1)
     with pytest.raises(ValueError, match="GPU tensor"):
         Z.zero_flatten_plan(Z.zero_shard_layout([8], 1, 0)[1], [x])
+
+
+def test_counts_beyond_a_buffer_are_refused_before_any_call():
+    """An element count larger than a tensor it describes is refused by the binding (the check on sizes comes
+    before the one on the device, so host tensors show it)."""
+    import torch
+
+    with pytest.raises(ValueError, match="the call touches 128"):
+        Z.zero_grad_sqnorm(torch.zeros(8, dtype=torch.bfloat16), Z.ZERO_BF16, 64, 256, 4096, 512, 520)
+    with pytest.raises(ValueError, match="the call touches 12288"):
+        Z.zero_adamw_step_tiled(16, Z.ZERO_BF16, torch.zeros(3 * 1024 - 1), 32, 8, lr=1e-3, beta1=0.9, beta2=0.999,
+                                eps=1e-8, weight_decay=0.0, grad_scale=1.0, step=1)
+    _, segs = Z.zero_shard_layout([8, 100], 1, 0)
+    with pytest.raises(ValueError, match="the call touches 200"):
+        Z.zero_flatten_plan(segs, [0, torch.zeros(99, dtype=torch.bfloat16)])
