@@ -278,7 +278,11 @@ int orc_loss_scale_update(double* scale, int32_t nonfinite, int32_t* good_steps,
  * functions above.  The simulated all-reduce sums the ranks' fp64 partial
  * square-norms in rank order and ORs their flags.  The grads hold g times
  * the loss scale, so the unscaled square-norm is global / scale²; the update
- * multiplies each gradient by coef / scale.  Overflow skips the update. */
+ * multiplies each gradient by coef / scale.  Overflow skips the update.
+ * Reading (the pages never reach it): a loss scale that is not a positive
+ * finite number, or so small that scale² underflows and a step without
+ * overflow has no finite unscaled norm, cannot give a decision: refused,
+ * nothing written. */
 int orc_step_decision(const double* rank_sqnorms, const int32_t* rank_flags, int32_t n_ranks, double max_norm,
                       double* loss_scale, int32_t* good_steps, int32_t growth_interval, double* grad_scale,
                       int32_t* skip, double* global_norm) {
@@ -293,6 +297,8 @@ int orc_step_decision(const double* rank_sqnorms, const int32_t* rank_flags, int
     if (rank_flags[r]) flag = 1;
   }
   double scale = *loss_scale;
+  if (!isfinite(scale)) return ORC_ERR_INVALID;
+  if (!flag && !isfinite(total / (scale * scale))) return ORC_ERR_INVALID;
   if (flag) {
     *skip = 1;
     *grad_scale = 0.0;
