@@ -1,17 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark: one data-parallel rank's ZeRO step on one MI355X.
 
-A step is the whole hot path on one rank's shard: shard layout (host, once),
-flatten of the per-tensor bf16 gradients into the rank's contiguous shard
+A step is the whole hot path on one rank's shard: shard layout (host),
+flatten of the per-tensor 16-bit gradients into the rank's contiguous shard
 fused with the fp64 gradient square-norm and the non-finite flag, the decision
 (clip coefficient, loss scale, skip) on one GPU thread (`--decision host`:
 on the host after a 16-byte readback), and the fused AdamW update of the fp32
 master/m/v shard with the bf16 parameter writeback.  Nothing in a default
 step waits on the host.
 
-Default workload: GPT-2 1.5B tensor list (48 layers, d=1600, ffn 6400, vocab
-50257, ctx 1024), N = 8 data-parallel ranks, rank 0's shard of 194,701,400
-parameters, synthetic bf16 gradients ~N(0, 1e-3) already resident in HBM.
+Default workload: the largest shard that fits one GPU, Llama-13B's tensor list
+(40 layers, d=5120, SwiGLU ffn 13824, vocab 32000), N = 4 data-parallel
+ranks, rank 0's shard of 3,253,966,080 parameters (52 GB of model state),
+synthetic fp16 gradients ~N(0, 1e-3) stored multiplied by a dynamic loss
+scale of 65536 and unscaled inside the update, already resident in HBM.
+`--workload gpt2-1.5b | llama-7b | 1t-zero3` selects the other shard shapes.
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on
 the stream the kernels run on; the roofline entry is for the fused AdamW
@@ -42,7 +45,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gpt2-1.5b")
+    ap.add_argument("--workload", default="llama-13b")
+    ap.add_argument("--grad-format", choices=("workload", "bf16", "fp16"), default="workload",
+                    help="override the workload's gradient format (fp16 then takes a 65536 loss scale, bf16 none): "
+                         "separates the format's cost from the shard's size")
     ap.add_argument("--state", choices=("tiled", "arrays"), default="tiled",
                     help="optimizer-state layout: tiled master/m/v (default) or three separate arrays")
     ap.add_argument("--unfused", action="store_true", help="flatten and square-norm as two passes")
@@ -59,14 +65,159 @@ def parse():
                          "(one-pass paths; the bucketed path uses one)")
     ap.add_argument("--producer", choices=("separate", "same"), default="separate",
                     help="with --produce: generate gradients on their own stream (default) or on the compute stream")
-    ap.add_argument("--event-every", type=int, default=10,
-                    help="bracket the kernels of every k-th timed step with HIP events (each record costs ~3 us)")
+    ap.add_argument("--event-every", type=int, default=1,
+                    help="bracket the kernels of every k-th timed step with HIP events (each record costs a few us "
+                         "of GPU time: nothing next to a large shard's step, 1%% of the GPT-2 shard's)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-sample", type=int, default=0, help="elements of the shard the oracle times (0: all)")
     ap.add_argument("--cpu-steps", type=int, default=4, help="steps the oracle times")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run plain device copies of this many bytes (for HBM counter scaling)")
+    ap.add_argument("--rmw-calibration", action="store_true",
+                    help="only time the update's access pattern without its arithmetic (zero_calibrate_tiled_rmw) "
+                         "next to the update itself, on the workload's shard size")
+    ap.add_argument("--reps", type=int, default=20, help="repetitions per kernel in --rmw-calibration")
+    ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="only write profiles/traffic_adamw_tiled_kernel_<workload>.json from four rocprofv3 --pmc "
+                         "output directories: FETCH_SIZE and WRITE_SIZE of this benchmark's command, and of "
+                         "--copy-calibration 1073741824 (the scale of each counter)")
     return ap.parse_args()
+
+
+def _counter_rows(d: str):
+    """(kernel name, counter value) of every dispatch in a rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {d}, found {files}")
+    with open(files[0]) as f:
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)]
+
+
+def traffic_record(args) -> None:
+    """Per-call HBM bytes of the tiled update from counter runs, each counter scaled by what it reads for a
+    plain 1 GiB device copy (the runtime's copy kernel; the average is over the 1 GiB copies only, not the
+    runtime's small uploads through the same kernel).  Tied to the SHA-256 of the kernel source."""
+    import hashlib
+
+    import mixed_precision_adam_amd as Z
+
+    w = workload(args)
+    lay, _ = Z.zero_shard_layout(w.numels, w.world, w.ranks[0])
+    n = lay.shard_numel
+    lpc = -(-n // (1 << 25))  # launches per update call
+    fetch, write, cfetch, cwrite = (_counter_rows(d) for d in args.traffic_record)
+    copy_kib = (1 << 30) / 1024
+
+    def copy_scale(rows):
+        vals = [v for k, v in rows if "copyBuffer" in k]
+        big = [v for v in vals if v > max(vals) / 2]
+        return copy_kib / (sum(big) / len(big))
+
+    fs, ws = copy_scale(cfetch), copy_scale(cwrite)
+    f = [v for k, v in fetch if "adamw_tiled_kernel" in k]
+    wr = [v for k, v in write if "adamw_tiled_kernel" in k]
+    if not f or len(f) % lpc or len(wr) % lpc:
+        raise SystemExit(f"{len(f)} / {len(wr)} update dispatches is not a whole number of {lpc}-launch calls")
+    fk, wk = sum(f) / (len(f) // lpc), sum(wr) / (len(wr) // lpc)
+    src = os.path.join(ROOT, "mixed_precision_adam_amd", "csrc", "zero_shard.hip")
+    rec = {"kernel": "adamw_tiled_kernel", "workload": w.name, "shard_numel": n, "launches_per_call": lpc,
+           "calls_counted": len(f) // lpc, "fetch_kib_raw_per_call": fk, "write_kib_raw_per_call": wk,
+           "fetch_scale": fs, "write_scale": ws, "bytes_per_call": (fk * fs + wk * ws) * 1024,
+           "algorithmic_bytes": ADAM_BYTES_PER_PARAM * n,
+           "source_sha256": hashlib.sha256(open(src, "rb").read()).hexdigest(),
+           "source": "mixed_precision_adam_amd/csrc/zero_shard.hip",
+           "summary": f"profiles/hbm_traffic_{w.name}.md"}
+    out = os.path.join(ROOT, "profiles", f"traffic_adamw_tiled_kernel_{w.name}.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def workload(args):
+    """The named workload, with its gradient format overridden by --grad-format."""
+    import dataclasses
+
+    import synth
+    from synth.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    if args.grad_format == "bf16" and w.grad_kind != synth.BF16:
+        w = dataclasses.replace(w, grad_kind=synth.BF16, loss_scale=1.0, inject={})
+    elif args.grad_format == "fp16" and w.grad_kind != synth.FP16:
+        w = dataclasses.replace(w, grad_kind=synth.FP16, loss_scale=65536.0, inject={})
+    return w
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def rmw_calibration(args) -> None:
+    """The update's ceiling on one shard: zero_calibrate_tiled_rmw (the tiled update's exact loads and stores,
+    the arithmetic replaced by an XOR with 0) and the update itself, alternating on the same buffers of the
+    workload's shard size, each timed with HIP events over `reps` back-to-back calls on torch's stream.
+    Prints both rates at the update's 28 bytes per element and their ratio."""
+    import torch
+
+    import mixed_precision_adam_amd as Z
+    import synth
+
+    w = workload(args)
+    dev = torch.device("cuda:0")
+    lay, _ = Z.zero_shard_layout(w.numels, w.world, w.ranks[0])
+    n = lay.shard_numel
+    dt16 = torch.bfloat16 if w.grad_kind == synth.BF16 else torch.float16
+    gdt = Z.ZERO_BF16 if w.grad_kind == synth.BF16 else Z.ZERO_FP16
+    grad = torch.zeros(n, dtype=dt16, device=dev)
+    synth.fill_tensor(w.grad_field(1), lay.shard_offset, grad[:lay.shard_valid])
+    state = torch.zeros(Z.zero_state_tiled_numel(n), dtype=torch.float32, device=dev)
+    master = torch.zeros(n, dtype=torch.float32, device=dev)
+    synth.fill_tensor(w.master_field(), lay.shard_offset, master[:lay.shard_valid])
+    zeros = torch.zeros(n, dtype=torch.float32, device=dev)
+    Z.zero_state_tile(master, zeros, zeros, state, n)
+    del master, zeros
+    param = torch.zeros(n, dtype=torch.bfloat16, device=dev)
+    hp = dict(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay,
+              grad_scale=1.0 / w.loss_scale, step=1)
+
+    def calib():
+        Z.zero_calibrate_tiled_rmw(grad, state, param, n, 0)
+
+    def update():
+        Z.zero_adamw_step_tiled(grad, gdt, state, param, n, **hp)
+
+    def timed(f) -> float:
+        f()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.reps):
+            f()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) * 1e-3 / args.reps
+
+    rounds = []
+    for _ in range(3):  # alternate, so slow drift of the box affects both alike
+        rounds.append((timed(calib), timed(update)))
+    c = sorted(r[0] for r in rounds)[1]
+    u = sorted(r[1] for r in rounds)[1]
+    launches = -(-n // (1 << 25))
+    print(json.dumps({"rmw_calibration": w.name, "grad_format": "bf16" if gdt == Z.ZERO_BF16 else "fp16",
+                      "shard_numel": n, "launches_per_call": launches, "reps": args.reps,
+                      "rmw_ms": c * 1e3, "rmw_gbs": ADAM_BYTES_PER_PARAM * n / c / 1e9,
+                      "update_ms": u * 1e3, "update_gbs": ADAM_BYTES_PER_PARAM * n / u / 1e9,
+                      "update_over_rmw": c / u, "rounds_ms": [[a * 1e3, b * 1e3] for a, b in rounds]}))
 
 
 def copy_calibration(nbytes: int, reps: int = 10) -> None:
@@ -174,6 +325,12 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.rmw_calibration:
+        rmw_calibration(args)
+        return
+    if args.traffic_record:
+        traffic_record(args)
+        return
 
     import torch
 
@@ -181,9 +338,8 @@ def main():
     import synth
     from mixed_precision_adam_amd.driver import (AdamWConfig, BucketPipeline, DeviceDecision, RankShard,
                                                  ScalerState, wait_spin)
-    from synth.workloads import WORKLOADS
 
-    w = WORKLOADS[args.workload]
+    w = workload(args)
     # Gradients generated straight into the shard (the 1T ZeRO-3 shard): no per-tensor sources, no flatten;
     # the step is square-norm -> decision -> update.
     flat = w.flat_shard_only
@@ -337,7 +493,7 @@ def main():
             sh.sqnorm(stream)                          # a3
         if e:
             e[3].record(stream)
-        sh.readback()                                  # 16 bytes to the host
+        sh.readback(stream)                            # 16 bytes to the host
         wait_spin(stream)
         sq, fl = sh.norm_result()                      # a4: host decision
         dec = Z.zero_step_decision([sq], [fl], cfg.max_norm, scaler.scale, scaler.good_steps,
@@ -415,7 +571,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": adam_gbs / HBM_PEAK_GBS,
-            "traffic": measured_traffic("adamw_tiled_kernel" if sh.tiled else "adamw_vec_kernel", w.name),
+            "traffic": measured_traffic("adamw_tiled_kernel" if sh.tiled else "adamw_vec_kernel", w.name)
+            if args.grad_format == "workload" else None,
             "bytes_per_param": ADAM_BYTES_PER_PARAM,
             "per": "update call: the shard in launches of at most 2^25 elements, timed together",
         },
@@ -444,6 +601,7 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample, args.cpu_steps)
         result["cpu_baseline"]["host_cores_available"] = os.cpu_count()
+        result["cpu_baseline"]["cpu_model"] = cpu_model()
     print(json.dumps(result))
 
 

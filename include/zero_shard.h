@@ -229,7 +229,11 @@ int zero_grad_sqnorm(const void* shard_dev, zero_dtype dt, int64_t n, void* ws_d
  *         *grad_scale = coef / loss_scale; then growth_interval consecutive
  *         good steps double *loss_scale.
  * *global_norm receives the unscaled norm (NaN/inf when skipped).  For bf16
- * training pass loss_scale = 1 and growth_interval = INT32_MAX. */
+ * training pass loss_scale = 1 and growth_interval = INT32_MAX.
+ * A loss scale that is not a positive finite number, or one so small that
+ * loss_scale² underflows and the unscaled square-norm of a step without
+ * overflow is not finite (after a long run of halvings), is refused with
+ * ZERO_ERR_INVALID and nothing is written. */
 int zero_step_decision(const double* rank_sqnorms, const int32_t* rank_flags, int32_t n_ranks, double max_norm,
                        double* loss_scale, int32_t* good_steps, int32_t growth_interval, double* grad_scale,
                        int32_t* skip, double* global_norm);
@@ -323,12 +327,20 @@ typedef struct zero_step_state {
   int32_t good_steps;     /* consecutive good steps since the last scale change */
   int32_t growth_interval;
   int32_t skip;           /* 1: the last decided step is skipped (the update kernels do nothing) */
-  int32_t reserved;
+  int32_t error;          /* 0, or ZERO_STEP_ERR_LOSS_SCALE for the last decided step */
   float scalars[12];      /* fp32 b1, 1-b1, b2, 1-b2, eps, 1-lr*wd, lr/(1-b1^t), sqrt(1-b2^t), gscale, 0, 0, 0 */
 } zero_step_state;
 
-/* Device.  Writes the initial state (loss scale, growth interval >= 1, t = 0)
- * with a one-thread kernel.  state_dev: 16-byte aligned. */
+/* The decision could not be taken: the loss scale is not a positive finite
+ * number, or loss_scale² underflowed so that the unscaled square-norm of a
+ * step without overflow is not finite (the cases zero_step_decision refuses
+ * with ZERO_ERR_INVALID).  The step is skipped (skip = 1, grad_scale = 0,
+ * global_norm = NaN); loss scale, good steps and Adam t are left as they
+ * are.  The next decision sets error back to 0 if it can be taken. */
+#define ZERO_STEP_ERR_LOSS_SCALE 1
+
+/* Device.  Writes the initial state (loss scale, growth interval >= 1, t = 0,
+ * error 0) with a one-thread kernel.  state_dev: 16-byte aligned. */
 int zero_step_state_init(zero_step_state* state_dev, double loss_scale, int32_t growth_interval, void* stream);
 
 /* Device.  rank_sqnorms_dev[n_ranks] (double) and rank_flags_dev[n_ranks]
@@ -347,6 +359,23 @@ int zero_adamw_step_dev(const void* grad_dev, zero_dtype gdt, float* master_dev,
                         void* stream);
 int zero_adamw_step_tiled_dev(const void* grad_dev, zero_dtype gdt, float* state_dev, uint16_t* param_dev,
                               zero_dtype pdt, int64_t n, const zero_step_state* step_state_dev, void* stream);
+
+/* ------------------------------------------------------------------ measurement aid
+ *
+ * Not a step of the method: the read-modify-write ceiling of the tiled
+ * update's own access pattern.  Device.  Exactly the loads and stores of
+ * zero_adamw_step_tiled over n elements (same launches of at most 2^25
+ * elements, same workgroup-to-tile mapping, same non-temporal hints: read 2 B
+ * of gradient and 12 B of tiled state, write the 12 B of state back and 2 B
+ * of parameter per element), with the arithmetic replaced by an XOR with key:
+ * state words become state ^ key, each 32-bit pair of parameters becomes the
+ * gradient pair ^ key.  With key = 0 the state keeps its bits and the
+ * parameters receive the gradient bits.  Only whole groups of four elements
+ * are touched (n mod 4 trailing elements are left alone).  Same alignment
+ * rules as the vector path of zero_adamw_step_tiled (grad and param 8-byte,
+ * state 16-byte aligned), otherwise ZERO_ERR_INVALID. */
+int zero_calibrate_tiled_rmw(const void* grad_dev, float* state_dev, uint16_t* param_dev, int64_t n, uint32_t key,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -282,14 +282,13 @@ __device__ __forceinline__ int64_t xcd_grouped(int64_t b, int64_t n) {
 constexpr int64_t kTile4 = kTile / 4;  // 16-byte vectors per array per tile
 static_assert(kTile4 == kBlock * kTileUnits, "each thread owns kTileUnits groups of 4 elements of a tile");
 
-// At most 4 wavefronts per SIMD (4 tiles, 64 KiB in flight per CU): the
-// compiler reserves registers so that no more fit.  Measured on MI355X: 1.7%
-// faster than the 8 the kernel's 26 registers would allow (3: the same; 5:
-// 0.6% slower than 4; 2: 7% slower), 1% faster on the Llama-13B shard.
-template <int DT, int PT>
-STREAMING_KERNEL void adamw_tiled_kernel(const uint16_t* __restrict__ grad16, f32x4* __restrict__ state,
-                                         uint16_t* __restrict__ param16, int64_t n, int64_t tile0, AdamScalars s,
-                                         const zero_step_state* dev) {
+// One tile of the tiled update, or (CALIB) the same loads and stores with the
+// arithmetic replaced by an XOR with a run-time key: the read-modify-write
+// ceiling of exactly this access pattern (zero_calibrate_tiled_rmw).
+template <int DT, int PT, bool CALIB>
+__device__ __forceinline__ void tiled_tile(const uint16_t* __restrict__ grad16, f32x4* __restrict__ state,
+                                           uint16_t* __restrict__ param16, int64_t n, int64_t tile0, AdamScalars s,
+                                           const zero_step_state* dev, uint32_t key) {
   const int64_t tile = tile0 + xcd_grouped(blockIdx.x, gridDim.x);
   f32x4* base = state + tile * (3 * kTile4);
   u32x2 g[kTileUnits];
@@ -307,22 +306,50 @@ STREAMING_KERNEL void adamw_tiled_kernel(const uint16_t* __restrict__ grad16, f3
   }
   // The data loads above do not depend on the scalars, so they are in flight
   // while the (device-resident) scalars arrive.
-  if (!take_scalars(dev, s)) return;
+  if (!CALIB && !take_scalars(dev, s)) return;
 #pragma unroll
   for (int u = 0; u < kTileUnits; ++u) {
     const int j = threadIdx.x + u * kBlock;
     const int64_t e = tile * kTile + 4 * static_cast<int64_t>(j);
     if (e + 4 <= n) {
-      const u32x2 q = adam_unit4<DT, PT>(g[u], p[u], m[u], v[u], s);
+      u32x2 q;
+      if constexpr (CALIB) {
+        const u32x4 k4 = {key, key, key, key};
+        p[u] = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, p[u]) ^ k4);
+        m[u] = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, m[u]) ^ k4);
+        v[u] = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, v[u]) ^ k4);
+        q = g[u] ^ u32x2{key, key};
+      } else {
+        q = adam_unit4<DT, PT>(g[u], p[u], m[u], v[u], s);
+      }
       st_stream(base + j, p[u]);
       st_stream(base + kTile4 + j, m[u]);
       st_stream(base + 2 * kTile4 + j, v[u]);
       st_stream(reinterpret_cast<u32x2*>(param16 + e), q);
-    } else if (e < n) {
+    } else if (e < n && !CALIB) {
       float* f = reinterpret_cast<float*>(base + j);
       adam_partial4<DT, PT>(grad16, f, f + kTile, f + 2 * kTile, param16, e, n, s);
     }
   }
+}
+
+// At most 4 wavefronts per SIMD (4 tiles, 64 KiB in flight per CU): the
+// compiler reserves registers so that no more fit.  Measured on MI355X: 1.7%
+// faster than the 8 the kernel's 26 registers would allow (3: the same; 5:
+// 0.6% slower than 4; 2: 7% slower), 1% faster on the Llama-13B shard.
+template <int DT, int PT>
+STREAMING_KERNEL void adamw_tiled_kernel(const uint16_t* __restrict__ grad16, f32x4* __restrict__ state,
+                                         uint16_t* __restrict__ param16, int64_t n, int64_t tile0, AdamScalars s,
+                                         const zero_step_state* dev) {
+  tiled_tile<DT, PT, false>(grad16, state, param16, n, tile0, s, dev, 0u);
+}
+
+// The update's memory traffic without its arithmetic (whole groups of four
+// only; a ragged tail is left alone).
+STREAMING_KERNEL void tiled_rmw_calibration_kernel(const uint16_t* __restrict__ grad16, f32x4* __restrict__ state,
+                                                   uint16_t* __restrict__ param16, int64_t n, int64_t tile0,
+                                                   uint32_t key) {
+  tiled_tile<ZERO_BF16, ZERO_BF16, true>(grad16, state, param16, n, tile0, AdamScalars{}, nullptr, key);
 }
 
 // Element paths for ragged tails and unaligned buffers: the same update, one
@@ -783,6 +810,20 @@ int launch_adamw_arrays(const char* fn, const void* grad_dev, int gdt, float* ma
   return ZERO_OK;
 }
 
+// Issues launch(t0, count) for each launch of the tiled update over n
+// elements: count tiles from tile t0, at most kUpdateElemsPerLaunch elements.
+template <typename F>
+int for_each_tiled_launch(int64_t n, const char* fn, F&& launch) {
+  const int64_t tiles = ceil_div(n, kTile);
+  constexpr int64_t kTilesPerLaunch = kUpdateElemsPerLaunch / kTile;
+  for (int64_t t0 = 0; t0 < tiles; t0 += kTilesPerLaunch) {
+    launch(t0, std::min(kTilesPerLaunch, tiles - t0));
+    const int rc = launch_status(fn);
+    if (rc != ZERO_OK) return rc;
+  }
+  return ZERO_OK;
+}
+
 int launch_adamw_tiled(const char* fn, const void* grad_dev, int gdt, float* state_dev, uint16_t* param_dev, int pdt,
                        int64_t n, const AdamScalars& s, const zero_step_state* dev, hipStream_t st) {
   if (n > 0 && !state_dev) return fail(ZERO_ERR_INVALID, "%s: NULL state", fn);
@@ -791,20 +832,14 @@ int launch_adamw_tiled(const char* fn, const void* grad_dev, int gdt, float* sta
   const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
   if (!aligned8(grad_dev) || !aligned8(param_dev))
     return launch_elements<true>(g, gdt, state_dev, state_dev, state_dev, param_dev, pdt, 0, n, s, dev, st, fn);
-  const int64_t tiles = ceil_div(n, kTile);
   auto* state = reinterpret_cast<f32x4*>(state_dev);
-  constexpr int64_t kTilesPerLaunch = kUpdateElemsPerLaunch / kTile;
-  for (int64_t t0 = 0; t0 < tiles; t0 += kTilesPerLaunch) {
-    const int64_t cnt = std::min(kTilesPerLaunch, tiles - t0);
+  return for_each_tiled_launch(n, fn, [&](int64_t t0, int64_t cnt) {
     with_formats(gdt, pdt, [&](auto fm) {
       using FM = decltype(fm);
       hipLaunchKernelGGL((adamw_tiled_kernel<FM::grad, FM::param>), dim3(static_cast<unsigned>(cnt)), dim3(kBlock), 0,
                          st, g, state, param_dev, n, t0, s, dev);
     });
-    const int rc = launch_status(fn);
-    if (rc != ZERO_OK) return rc;
-  }
-  return ZERO_OK;
+  });
 }
 
 int dev_args_ok(const char* fn, const void* grad_dev, int gdt, const void* param_dev, int pdt, int64_t n,
@@ -829,7 +864,7 @@ __global__ void step_state_init_kernel(zero_step_state* st, double loss_scale, i
   st->good_steps = 0;
   st->growth_interval = growth_interval;
   st->skip = 1;  // nothing decided yet: an update launched now does nothing
-  st->reserved = 0;
+  st->error = 0;
   for (int k = 0; k < 12; ++k) st->scalars[k] = 0.0f;
 }
 
@@ -847,6 +882,18 @@ __global__ void step_decision_kernel(const double* __restrict__ sq, const int32_
   }
   const double scale = st->loss_scale;
   st->iteration += 1;
+  // The host decision refuses these cases with ZERO_ERR_INVALID; here the
+  // step is skipped, the error recorded, and the scale, good-step count and
+  // Adam t are left as they are.
+  const double unscaled = global / (scale * scale);
+  if (!(scale > 0.0) || !isfinite(scale) || (!overflow && !isfinite(unscaled))) {
+    st->skip = 1;
+    st->error = ZERO_STEP_ERR_LOSS_SCALE;
+    st->grad_scale = 0.0;
+    st->global_norm = __builtin_nan("");
+    return;
+  }
+  st->error = 0;
   if (overflow) {
     st->skip = 1;
     st->grad_scale = 0.0;
@@ -855,7 +902,6 @@ __global__ void step_decision_kernel(const double* __restrict__ sq, const int32_
     st->good_steps = 0;
     return;
   }
-  const double unscaled = global / (scale * scale);
   double coef = 1.0;
   if (max_norm > 0.0) {
     const double c = max_norm / (sqrt(unscaled) + 1e-6);
@@ -945,6 +991,19 @@ int norm_outputs_ok(const char* fn, int64_t n, const void* ws_dev, size_t ws_byt
   const size_t need = zero_grad_sqnorm_workspace_bytes(n);
   if (ws_bytes < need) return fail(ZERO_ERR_INVALID, "%s: workspace %zu bytes < %zu", fn, ws_bytes, need);
   return ZERO_OK;
+}
+
+// The fused flatten and its fold, with the partials in ws_dev (validated by
+// the caller to hold zero_grad_sqnorm_workspace_bytes(shard_numel) bytes).
+int flatten_sqnorm_into(const char* fn, const zero_flat_seg* segs_dev, int32_t n_segs, int dt, void* shard_dev,
+                        int64_t shard_numel, void* ws_dev, double* sqnorm_dev, int32_t* nonfinite_dev,
+                        hipStream_t st) {
+  const int64_t blocks = zero_flatten_partials_count(shard_numel);
+  double* part_sum = static_cast<double*>(ws_dev);
+  uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sum + (blocks > 0 ? blocks : 1));
+  int rc = launch_flatten_partials(fn, segs_dev, n_segs, dt, shard_dev, shard_numel, part_sum, part_bad, st);
+  if (rc != ZERO_OK) return rc;
+  return launch_fold(fn, part_sum, part_bad, blocks, sqnorm_dev, nonfinite_dev, st);
 }
 
 }  // namespace
@@ -1065,14 +1124,8 @@ int zero_flatten_grads_sqnorm(const zero_flat_seg* segs_dev, int32_t n_segs, zer
   if (rc != ZERO_OK) return rc;
   rc = norm_outputs_ok("zero_flatten_grads_sqnorm", shard_numel, ws_dev, ws_bytes, sqnorm_dev, nonfinite_dev);
   if (rc != ZERO_OK) return rc;
-  const int64_t blocks = zero_flatten_partials_count(shard_numel);
-  double* part_sum = static_cast<double*>(ws_dev);
-  uint32_t* part_bad = reinterpret_cast<uint32_t*>(part_sum + (blocks > 0 ? blocks : 1));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = launch_flatten_partials("zero_flatten_grads_sqnorm (flatten)", segs_dev, n_segs, dt, shard_dev, shard_numel,
-                               part_sum, part_bad, st);
-  if (rc != ZERO_OK) return rc;
-  return launch_fold("zero_flatten_grads_sqnorm (fold)", part_sum, part_bad, blocks, sqnorm_dev, nonfinite_dev, st);
+  return flatten_sqnorm_into("zero_flatten_grads_sqnorm", segs_dev, n_segs, dt, shard_dev, shard_numel, ws_dev,
+                             sqnorm_dev, nonfinite_dev, static_cast<hipStream_t>(stream));
 }
 
 int64_t zero_flatten_partials_count(int64_t numel) {
@@ -1175,12 +1228,15 @@ int zero_step_decision(const double* rank_sqnorms, const int32_t* rank_flags, in
     overflow = overflow || rank_flags[r] != 0;
   }
   const double scale = *loss_scale;
+  const double unscaled = global / (scale * scale);
+  if (!std::isfinite(scale) || (!overflow && !std::isfinite(unscaled)))
+    return fail(ZERO_ERR_INVALID, "zero_step_decision: loss scale %g is not usable (the unscaled square-norm is %g)",
+                scale, unscaled);
   if (overflow) {
     *skip = 1;
     *grad_scale = 0.0;
     *global_norm = std::numeric_limits<double>::quiet_NaN();
   } else {
-    const double unscaled = global / (scale * scale);
     *skip = 0;
     *grad_scale = zero_clip_coef(unscaled, max_norm) / scale;
     *global_norm = std::sqrt(unscaled);
@@ -1277,6 +1333,22 @@ int zero_state_untile(const float* state_dev, float* master_dev, float* m_dev, f
   hipLaunchKernelGGL(retile_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(kBlock), 0,
                      static_cast<hipStream_t>(stream), master_dev, m_dev, v_dev, const_cast<float*>(state_dev), n);
   return launch_status("zero_state_untile");
+}
+
+int zero_calibrate_tiled_rmw(const void* grad_dev, float* state_dev, uint16_t* param_dev, int64_t n, uint32_t key,
+                             void* stream) {
+  const char* fn = "zero_calibrate_tiled_rmw";
+  if (n < 0 || n > kMaxPsi || (n > 0 && (!grad_dev || !state_dev || !param_dev)) || !aligned8(grad_dev) ||
+      !aligned8(param_dev) || !aligned16(state_dev))
+    return fail(ZERO_ERR_INVALID, "%s: bad arguments", fn);
+  if (n == 0) return ZERO_OK;
+  const uint16_t* g = static_cast<const uint16_t*>(grad_dev);
+  auto* state = reinterpret_cast<f32x4*>(state_dev);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return for_each_tiled_launch(n, fn, [&](int64_t t0, int64_t cnt) {
+    hipLaunchKernelGGL(tiled_rmw_calibration_kernel, dim3(static_cast<unsigned>(cnt)), dim3(kBlock), 0, st, g, state,
+                       param_dev, n, t0, key);
+  });
 }
 
 }  // extern "C"

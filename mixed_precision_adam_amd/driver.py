@@ -137,9 +137,12 @@ class RankShard:
         zero_grad_sqnorm(self.grad, self.grad_dtype, self.n, self.ws, self.ws_bytes, self.sq_dev, self.flag_dev,
                          stream)
 
-    def readback(self) -> None:
-        """Queue the 16-byte copy of the square-norm and flag to pinned host memory."""
-        self.norm_host.copy_(self.norm_dev, non_blocking=True)
+    def readback(self, stream=None) -> None:
+        """Queue the 16-byte copy of the square-norm and flag to pinned host memory on `stream` (the stream
+        the norm ran on, so the copy is ordered after it and a wait on that stream covers both)."""
+        stream = stream or torch.cuda.current_stream()
+        with torch.cuda.stream(stream):
+            self.norm_host.copy_(self.norm_dev, non_blocking=True)
 
     def norm_result(self):
         """Host copies of the last sqnorm; call after the stream has been synchronized."""
@@ -304,7 +307,7 @@ def rank_norms(shards, cfg: AdamWConfig, scaler: ScalerState, flatten: bool = Tr
             sh.flatten(stream)
         if not (flatten and sh.fused):
             sh.sqnorm(stream)
-        sh.readback()
+        sh.readback(stream)
     wait_spin(stream)
     sq, fl = zip(*(sh.norm_result() for sh in shards))
     dec = zero_step_decision(sq, fl, cfg.max_norm, scaler.scale, scaler.good_steps, scaler.growth_interval)

@@ -279,3 +279,27 @@ def test_counts_beyond_a_buffer_are_refused_before_any_call():
     _, segs = Z.zero_shard_layout([8, 100], 1, 0)
     with pytest.raises(ValueError, match="the call touches 200"):
         Z.zero_flatten_plan(segs, [0, torch.zeros(99, dtype=torch.bfloat16)])
+
+
+def test_unusable_loss_scale_is_refused_by_host_decision_and_oracle():
+    """A loss scale that is not a positive finite number, or one whose square underflows so that a step
+    without overflow has no finite unscaled norm, gives no decision on either side (reading: the pages never
+    reach this case).  An overflow at a tiny positive scale is an ordinary skip: the scale halves, to 0 from
+    the smallest positive double."""
+    for scale, flag in ((0.0, 0), (0.0, 1), (-1.0, 0), (float("inf"), 0), (float("inf"), 1), (float("nan"), 0),
+                        (5e-324, 0), (1e-170, 0)):
+        with pytest.raises(Z.ZeroError):
+            Z.zero_step_decision([2.5], [flag], 1.0, scale, 0, 1000)
+        with pytest.raises(oracle.OracleError):
+            oracle.step_decision([2.5], [flag], 1.0, scale, 0, 1000)
+    for scale in (5e-324, 1e-170):
+        got = Z.zero_step_decision([2.5], [1], 1.0, scale, 3, 1000)
+        ref = oracle.step_decision([2.5], [1], 1.0, scale, 3, 1000)
+        assert got["skip"] == ref["skip"] == 1 and got["loss_scale"] == ref["loss_scale"] == scale * 0.5
+        assert got["good_steps"] == ref["good_steps"] == 0
+    assert 5e-324 * 0.5 == 0.0
+    # the smallest scales that still give a finite unscaled norm are decided normally, the same on both sides
+    for scale in (1e-150, 2.0**-537):
+        got = Z.zero_step_decision([2.5e-300], [0], 1.0, scale, 0, 1000)
+        ref = oracle.step_decision([2.5e-300], [0], 1.0, scale, 0, 1000)
+        assert got == ref and got["skip"] == 0 and math.isfinite(got["grad_scale"])

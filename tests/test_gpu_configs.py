@@ -73,6 +73,17 @@ def host_shard_grads(w, field, lay, inject_at=None):
     return g
 
 
+def host_shard_grads_window(w, field, lay, a, b, inject_at=None):
+    """Shard elements [a, b) of host_shard_grads, generated for the window alone."""
+    g = np.zeros(b - a, dtype=np.uint16)
+    va = min(b, lay.shard_valid)
+    if va > a:
+        synth.fill_host(field, lay.shard_offset + a, va - a, out=g[:va - a])
+    if inject_at is not None and a <= inject_at[0] < b:
+        g[inject_at[0] - a] = inject_at[1]
+    return g
+
+
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["gpt2-1.5b", "llama-7b", "llama-13b", "1t-zero3"])
 def test_config_parity(name):
@@ -183,32 +194,42 @@ def test_config_parity(name):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("bucket", [0, 1 << 25])
-def test_benchmark_path_parity_gpt2(bucket):
-    """The GPT-2 1.5B rank shard exactly as `bench.py` steps it: fused flatten + norm (in one pass, or in
-    constant-capacity buckets of 2^25 elements, last first), the decision on the device, the tiled update in
-    launches of 2^25 elements.  The GPU takes its own decision here; the oracle takes its own, and the states
-    must agree bit for bit whenever the two fp32 factors coincide (within tolerance otherwise)."""
+@pytest.mark.parametrize("name,bucket", [("gpt2-1.5b", 0), ("gpt2-1.5b", 1 << 25), ("llama-13b", 0)])
+def test_benchmark_path_parity(name, bucket):
+    """A rank shard exactly as `bench.py` steps it: fused flatten + norm (in one pass, or in constant-capacity
+    buckets of 2^25 elements, last first), the decision on the device, the tiled update in launches of 2^25
+    elements.  GPT-2 1.5B (bf16) and Llama-13B (the benchmark's default: fp16 gradients stored multiplied by
+    a dynamic loss scale that starts at 65536, +inf injected at step 2 and -inf at step 5, so the device
+    skips those steps and halves the scale: 65536 -> 32768 -> 16384 over 4 Adam steps).  The GPU takes its
+    own decision; the oracle takes its own.  Skip, loss scale, good steps and Adam t must agree exactly and
+    the factor within the bound of two fp64 summation orders (several factors are correct).  The update given
+    a factor is unique, so the oracle then applies the device's factor and the sampled states must agree bit
+    for bit; a skipped step must leave every sampled byte as it was."""
     from mixed_precision_adam_amd.driver import BucketPipeline, DeviceDecision
 
-    w = WORKLOADS["gpt2-1.5b"]
+    w = WORKLOADS[name]
     dev = torch.device("cuda:0")
     rank = w.ranks[0]
+    gdt = Z.ZERO_BF16 if w.grad_kind == synth.BF16 else Z.ZERO_FP16
+    tdt = torch.bfloat16 if gdt == Z.ZERO_BF16 else torch.float16
+    growth = 1000 if gdt == Z.ZERO_FP16 else 2**31 - 1
     lay, segs = Z.zero_shard_layout(w.numels, w.world, rank)
     starts = np.cumsum([0] + list(w.numels))
     sources = [None] * len(w.numels)
     for sg in segs:
-        sources[sg.tensor] = torch.empty(w.numels[sg.tensor], dtype=torch.bfloat16, device=dev)
-    sh = RankShard(w.numels, w.world, rank, Z.ZERO_BF16, dev, sources=sources, tiled=True, fused=True)
+        sources[sg.tensor] = torch.empty(w.numels[sg.tensor], dtype=tdt, device=dev)
+    sh = RankShard(w.numels, w.world, rank, gdt, dev, sources=sources, tiled=True, fused=True)
     S = sh.n
     master0 = torch.zeros(S, dtype=torch.float32, device=dev)
     synth.fill_tensor(w.master_field(), lay.shard_offset, master0[:lay.shard_valid])
     sh.load_master(master0)
     del master0
     cfg = AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, max_norm=w.clip)
-    runner = BucketPipeline(sh, sources, bucket, cfg) if bucket else DeviceDecision([sh], cfg)
     if bucket:
+        runner = BucketPipeline(sh, sources, bucket, cfg, loss_scale=w.loss_scale, growth_interval=growth)
         assert len(runner.windows) == -(-S // bucket)
+    else:
+        runner = DeviceDecision([sh], cfg, loss_scale=w.loss_scale, growth_interval=growth)
     wins = windows(lay, segs)
     if bucket:  # the seams between buckets too
         wins = sorted(set(wins) | {(max(0, k * bucket - WIN // 2), min(S, k * bucket + WIN // 2))
@@ -221,29 +242,55 @@ def test_benchmark_path_parity_gpt2(bucket):
             synth.fill_host(w.master_field(), lay.shard_offset + a, va - a, out=p[:va - a])
         ref.append([p, np.zeros(b - a, np.float32), np.zeros(b - a, np.float32), np.zeros(b - a, np.uint16)])
     torch.cuda.synchronize()
+    oscale, ogood, ostep, skips = w.loss_scale, 0, 0, 0
     for t in range(1, w.steps + 1):
-        print(f"[gpt2 bucket={bucket}] step {t}", flush=True)
-        field = w.grad_field(t)
+        print(f"[{name} bucket={bucket}] step {t}", flush=True)
+        field = w.grad_field(t, oscale)  # gradients stored multiplied by the scale in force
         for sg in segs:
             synth.fill_tensor(field, int(starts[sg.tensor]), sources[sg.tensor])
+        inject_at = None
+        if t in w.inject:
+            val, frac = w.inject[t]
+            j = int(frac * lay.shard_valid)
+            bits = np.array([val], dtype=np.float16 if gdt == Z.ZERO_FP16 else np.float32)
+            hb = int(bits.view(np.uint16)[0]) if gdt == Z.ZERO_FP16 else int(bits.view(np.uint32)[0] >> 16)
+            inject_at = (j, hb)
+            sg = next(x for x in segs if x.dst_offset <= j < x.dst_offset + x.numel)
+            sources[sg.tensor].view(torch.int16)[sg.src_offset + j - sg.dst_offset] = hb - (1 << 16 if hb >= 1 << 15
+                                                                                              else 0)
         runner.step()
         st = runner.read()
-        g_host = host_shard_grads(w, field, lay)
+        g_host = host_shard_grads(w, field, lay, inject_at)
         for a, b in wins:
-            assert_bits_equal(bits16(sh.grad[a:b]), g_host[a:b], f"bucket={bucket} step {t} shard [{a},{b})")
-        osq, oflag = oracle.sqnorm(g_host, Z.ZERO_BF16)
-        od = oracle.step_decision([osq], [oflag], w.clip, 1.0, 0, 2**31 - 1)
-        assert st["skip"] == od["skip"] == 0 and st["adam_step"] == t
-        assert_norm_close(st["global_norm"] ** 2, od["global_norm"] ** 2, S, f"bucket={bucket} step {t} norm")
-        same = assert_grad_scale_close(st["grad_scale"], od["grad_scale"], S, f"bucket={bucket} step {t}")
+            assert_bits_equal(bits16(sh.grad[a:b]), g_host[a:b], f"{name} bucket={bucket} step {t} shard [{a},{b})")
+        osq, oflag = oracle.sqnorm(g_host, gdt)
+        del g_host
+        od = oracle.step_decision([osq], [oflag], w.clip, oscale, ogood, growth)
+        oscale, ogood = od["loss_scale"], od["good_steps"]
+        what = f"{name} bucket={bucket} step {t}"
+        assert st["skip"] == od["skip"] and st["loss_scale"] == od["loss_scale"], (what, st, od)
+        assert st["good_steps"] == od["good_steps"] and st["error"] == 0 and st["iteration"] == t, (what, st)
+        if od["skip"]:
+            skips += 1
+        else:
+            ostep += 1
+            assert_norm_close(st["global_norm"] ** 2, od["global_norm"] ** 2, S, what + " norm")
+            # the device's factor is one of the correct ones (fp64 summation order) ...
+            assert_grad_scale_close(st["grad_scale"], od["grad_scale"], S, what)
+        assert st["adam_step"] == ostep, (what, st)
         nd = 0
         for (a, b), R in zip(wins, ref):
-            oracle.adamw_step(g_host[a:b].copy(), Z.ZERO_BF16, R[0], R[1], R[2], R[3], lr=w.lr, beta1=w.beta1,
-                              beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, grad_scale=od["grad_scale"],
-                              step=t)
+            if not od["skip"]:  # ... and the update given that factor is unique: the oracle applies it too
+                g_win = host_shard_grads_window(w, field, lay, a, b, inject_at)
+                oracle.adamw_step(g_win, gdt, R[0], R[1], R[2], R[3], lr=w.lr, beta1=w.beta1, beta2=w.beta2,
+                                  eps=w.eps, weight_decay=w.weight_decay, grad_scale=st["grad_scale"], step=ostep)
             gp, gm, gv = (x.cpu().numpy() for x in sh.state_views(a, b))
-            what = f"bucket={bucket} step {t} [{a},{b})"
-            nd += assert_f32_close(gp, R[0], what + " master") + assert_f32_close(gm, R[1], what + " m")
-            nd += assert_f32_close(gv, R[2], what + " v")
-            nd += assert_bf16_within_ulp(bits16(sh.param[a:b]), R[3], what + " param")
-        assert nd == 0 or not same, f"bucket={bucket} step {t}: {nd} sampled elements differ with equal factors"
+            ww = f"{what} [{a},{b})"
+            nd += assert_f32_close(gp, R[0], ww + " master") + assert_f32_close(gm, R[1], ww + " m")
+            nd += assert_f32_close(gv, R[2], ww + " v")
+            if ostep > 0:
+                nd += assert_bf16_within_ulp(bits16(sh.param[a:b]), R[3], ww + " param")
+        assert nd == 0, f"{what}: {nd} sampled elements differ in bits from the oracle given the same factor"
+    assert skips == len(w.inject)
+    if name == "llama-13b":
+        assert oscale == 16384.0 and ostep == 4
