@@ -24,8 +24,10 @@
  *     argument validation and kernel-launch errors only, not kernel results.
  *   - Memory: the caller allocates and frees every buffer (device buffers,
  *     workspace, segment tables).  The library never allocates or frees
- *     device memory and keeps no mutable global state besides the per-thread
- *     error message.
+ *     device memory.  Its only mutable global state is the per-thread error
+ *     message and, for zero_flatten_grads_sqnorm_noalloc, one fixed-size
+ *     scratch array per device (a static device variable) and its looked-up
+ *     device addresses.
  *   - Device calls are asynchronous: they enqueue kernels on `stream` (a
  *     hipStream_t; NULL = the default stream) and return before completion.
  *   - Device buffers passed to one call must not overlap unless stated.
@@ -170,6 +172,26 @@ int zero_flatten_grads(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype
 int zero_flatten_grads_sqnorm(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype dt, void* shard_dev,
                               int64_t shard_numel, void* ws_dev, size_t ws_bytes, double* sqnorm_dev,
                               int32_t* nonfinite_dev, void* stream);
+
+/* Device.  For callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same fused flatten and norm as zero_flatten_grads_sqnorm, with the same
+ * results bit for bit, but with its partials in a static scratch array of
+ * ZERO_NOALLOC_SCRATCH_BYTES (6 MiB) per device instead of a caller
+ * workspace.  That covers every shard size; a shard needing more scratch
+ * than the array holds would be refused with ZERO_ERR_CAPACITY.  It calls no
+ * allocating routine.  On its first call on a device the array's device
+ * address is looked up (hipGetSymbolAddress) with that device current, so
+ * call it with the stream's device current (a stream of another device is
+ * refused with ZERO_ERR_INVALID).  Every call on one device shares that
+ * device's array: calls that overlap in time on one device (two streams, two
+ * threads) race on it and give wrong sums; serialize them.  The array keeps
+ * the last call's partials; no call relies on its earlier contents (every
+ * partial is written before it is read).  sqnorm_dev: 8-byte aligned;
+ * nonfinite_dev: 4-byte aligned. */
+#define ZERO_NOALLOC_SCRATCH_BYTES ((size_t)6 << 20)
+int zero_flatten_grads_sqnorm_noalloc(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype dt, void* shard_dev,
+                                      int64_t shard_numel, double* sqnorm_dev, int32_t* nonfinite_dev, void* stream);
 
 /* Bucketed norm.  With the shard split into constant-capacity windows
  * (zero_bucket_segments), each window is flattened as soon as its gradients

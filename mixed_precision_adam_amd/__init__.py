@@ -103,6 +103,7 @@ _lib.zero_step_state_init.argtypes = [_P, C.c_double, C.c_int32, _P]
 _lib.zero_step_decision_dev.argtypes = [_P, _P, C.c_int32, C.c_double, C.POINTER(zero_adamw_hparams), _P, _P]
 _lib.zero_adamw_step_dev.argtypes = [_P, C.c_int, _P, _P, _P, _P, C.c_int, C.c_int64, _P, _P]
 _lib.zero_adamw_step_tiled_dev.argtypes = [_P, C.c_int, _P, _P, C.c_int, C.c_int64, _P, _P]
+_lib.zero_flatten_grads_sqnorm_noalloc.argtypes = [_P, C.c_int32, C.c_int, _P, C.c_int64, _P, _P, _P]
 _lib.zero_calibrate_tiled_rmw.argtypes = [_P, _P, _P, C.c_int64, C.c_uint32, _P]
 
 ZERO_STATE_TILE = 1024  # include/zero_shard.h
@@ -121,8 +122,9 @@ EXPORTS = ("zero_last_error", "zero_shard_layout", "zero_flatten_plan", "zero_bu
            "zero_clip_coef", "zero_loss_scale_update", "zero_cosine_lr", "zero_adamw_step", "zero_state_tiled_numel",
            "zero_adamw_step_tiled", "zero_state_tile", "zero_state_untile", "zero_step_state_init",
            "zero_step_decision_dev", "zero_adamw_step_dev", "zero_adamw_step_tiled_dev",
-           "zero_calibrate_tiled_rmw")
+           "zero_flatten_grads_sqnorm_noalloc", "zero_calibrate_tiled_rmw")
 ZERO_STEP_ERR_LOSS_SCALE = 1  # zero_step_state.error: the decision could not be taken
+ZERO_NOALLOC_SCRATCH_BYTES = 6 << 20  # static scratch of zero_flatten_grads_sqnorm_noalloc, per device
 
 
 def library() -> C.CDLL:
@@ -290,6 +292,13 @@ def zero_flatten_grads_sqnorm(segs_dev, n_segs: int, dtype: int, shard, shard_nu
     _check(_lib.zero_flatten_grads_sqnorm(_buf(segs_dev, _SEG * max(n_segs, 0)), n_segs, dtype,
                                           _buf(shard, 2 * max(shard_numel, 0)), shard_numel, _buf(ws, ws_bytes),
                                           ws_bytes, _buf(sqnorm_out, 8), _buf(nonfinite_out, 4), _stream(stream)))
+
+
+def zero_flatten_grads_sqnorm_noalloc(segs_dev, n_segs: int, dtype: int, shard, shard_numel: int, sqnorm_out,
+                                      nonfinite_out, stream=None) -> None:
+    _check(_lib.zero_flatten_grads_sqnorm_noalloc(_buf(segs_dev, _SEG * max(n_segs, 0)), n_segs, dtype,
+                                                  _buf(shard, 2 * max(shard_numel, 0)), shard_numel,
+                                                  _buf(sqnorm_out, 8), _buf(nonfinite_out, 4), _stream(stream)))
 
 
 def zero_calibrate_tiled_rmw(grad, state, param, n: int, key: int = 0, stream=None) -> None:

@@ -19,6 +19,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <limits>
+#include <mutex>
 
 #include "zero_shard.h"
 
@@ -1008,6 +1009,56 @@ int flatten_sqnorm_into(const char* fn, const zero_flat_seg* segs_dev, int32_t n
 
 }  // namespace
 
+// ------------------------------------------------------------------ static scratch
+//
+// For callers that cannot allocate: the partials of the fused flatten + norm
+// live in this file-scope array instead of a caller workspace.  Its size is
+// the largest workspace the fused flatten ever needs (2^19 partials of 12
+// bytes), so every shard size fits.  Every GPU the library runs on holds its
+// own copy until the process ends.  In host code `scratch` only names the
+// variable: its device address is looked up once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+constexpr size_t kStaticScratchBytes = ZERO_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kScratchMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call on that device.  The stream (if any) must belong to that device.
+int static_scratch(const char* fn, hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(ZERO_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kScratchMaxDevices)
+    return fail(ZERO_ERR_INVALID, "%s: device %d outside the %d devices the scratch table covers", fn, dev,
+                kScratchMaxDevices);
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(ZERO_ERR_HIP, "%s: hipStreamGetDevice failed: %s", fn, hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(ZERO_ERR_INVALID, "%s: the stream belongs to device %d, the current device is %d", fn,
+                  static_cast<int>(sdev), dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(ZERO_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return ZERO_OK;
+}
+
+}  // namespace
+
 // ====================================================================== C ABI
 
 extern "C" {
@@ -1126,6 +1177,24 @@ int zero_flatten_grads_sqnorm(const zero_flat_seg* segs_dev, int32_t n_segs, zer
   if (rc != ZERO_OK) return rc;
   return flatten_sqnorm_into("zero_flatten_grads_sqnorm", segs_dev, n_segs, dt, shard_dev, shard_numel, ws_dev,
                              sqnorm_dev, nonfinite_dev, static_cast<hipStream_t>(stream));
+}
+
+int zero_flatten_grads_sqnorm_noalloc(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype dt, void* shard_dev,
+                                      int64_t shard_numel, double* sqnorm_dev, int32_t* nonfinite_dev, void* stream) {
+  const char* fn = "zero_flatten_grads_sqnorm_noalloc";
+  int rc = flatten_args_ok(fn, segs_dev, n_segs, dt, shard_dev, shard_numel);
+  if (rc != ZERO_OK) return rc;
+  if (!sqnorm_dev || !nonfinite_dev || !aligned8(sqnorm_dev) || (reinterpret_cast<uintptr_t>(nonfinite_dev) & 3u))
+    return fail(ZERO_ERR_INVALID, "%s: outputs NULL or misaligned", fn);
+  const size_t need = zero_grad_sqnorm_workspace_bytes(shard_numel);
+  if (need > kStaticScratchBytes)
+    return fail(ZERO_ERR_CAPACITY, "%s: a shard of %lld elements needs %zu bytes of scratch, the static scratch holds %zu",
+                fn, static_cast<long long>(shard_numel), need, kStaticScratchBytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  rc = static_scratch(fn, st, &ws);
+  if (rc != ZERO_OK) return rc;
+  return flatten_sqnorm_into(fn, segs_dev, n_segs, dt, shard_dev, shard_numel, ws, sqnorm_dev, nonfinite_dev, st);
 }
 
 int64_t zero_flatten_partials_count(int64_t numel) {
