@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama-13b")
+    ap.add_argument("--prepend", type=int, default=0,
+                    help="put a tensor of this many elements in front of the workload's list: an odd count "
+                         "shifts every later tensor against the shard's 16-byte lines (the flatten's phase-shifted "
+                         "path)")
     ap.add_argument("--grad-format", choices=("workload", "bf16", "fp16"), default="workload",
                     help="override the workload's gradient format (fp16 then takes a 65536 loss scale, bf16 none): "
                          "separates the format's cost from the shard's size")
@@ -144,6 +148,8 @@ def workload(args):
     from synth.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
+    if args.prepend:
+        w = dataclasses.replace(w, numels=[args.prepend] + list(w.numels), name=f"{w.name}+{args.prepend}")
     if args.grad_format == "bf16" and w.grad_kind != synth.BF16:
         w = dataclasses.replace(w, grad_kind=synth.BF16, loss_scale=1.0, inject={})
     elif args.grad_format == "fp16" and w.grad_kind != synth.FP16:

@@ -156,9 +156,12 @@ int zero_bucket_segments(const zero_segment* segs, int32_t n_segs, int64_t win_b
  * dst_offset and non-overlapping, each inside [0, shard_numel).  Writes
  * shard[0, shard_numel): covered elements are bit copies of the source,
  * uncovered ones (padding) are +0.  Never writes outside the shard.  dt only
- * names the 16-bit format (the copy is bitwise). 16-byte aligned pieces with
- * matching source/destination phase take 16-byte vector copies; others are
- * copied element by element with the same result. */
+ * names the 16-bit format (the copy is bitwise).  The body of every piece
+ * moves 16-byte vectors to 16-byte aligned destinations; when source and
+ * destination differ in their position inside a 16-byte line, each vector is
+ * assembled from the two aligned source lines it straddles (reads never leave
+ * a 16-byte line that holds bytes of the piece).  Heads and tails shorter
+ * than a vector are copied element by element. */
 int zero_flatten_grads(const zero_flat_seg* segs_dev, int32_t n_segs, zero_dtype dt, void* shard_dev,
                        int64_t shard_numel, void* stream);
 

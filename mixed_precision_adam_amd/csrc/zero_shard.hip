@@ -572,44 +572,52 @@ __global__ __launch_bounds__(kBlock) void sqnorm_fold_chunks_kernel(double* __re
 
 // ------------------------------------------------------------------ flatten
 
-// A workgroup copies len 16-bit elements from s to d.  When both addresses
-// share their position inside a 16-byte line, a scalar head brings d to a
-// 16-byte boundary and the body moves 16-byte vectors.  With ACC the copied
-// values are also squared into acc (fp64) and checked for inf/NaN.  Source
-// reads stream (non-temporal); the shard is stored with ordinary stores: the
-// update reads part of it back from the Infinity Cache right away.  Measured
-// on MI355X against non-temporal stores: the GPT-2 1.5B rank's whole step is
-// 1.2% faster that way (its flatten 3.7%) and the Llama-13B one 0.8-1%,
-// although a plain copy runs 1-2% slower.
 // Source tensors are plain device allocations (global memory); saying so lets
 // the compiler use global rather than flat loads for them.
 typedef const u32x4 __attribute__((address_space(1)))* global_u32x4_ptr;
 typedef const uint16_t __attribute__((address_space(1)))* global_u16_ptr;
 
-template <int DT, bool ACC>
-__device__ void copy_piece(const uint16_t* __restrict__ s_generic, uint16_t* __restrict__ d, int64_t len, double& acc,
-                           uint32_t& bad) {
-  const global_u16_ptr s = (global_u16_ptr)s_generic;
-  const uintptr_t ds = reinterpret_cast<uintptr_t>(d), ss = reinterpret_cast<uintptr_t>(s_generic);
-  int64_t head = len, nv = 0;
-  if (((ds ^ ss) & 15u) == 0) {
-    head = static_cast<int64_t>(((16u - (ds & 15u)) & 15u) >> 1);
-    if (head > len) head = len;
-    nv = (len - head) >> 3;
+// Bytes [SH, SH + 16) of the 32 bytes a, b (SH even, 2 .. 14): the 16 source
+// bytes of one destination vector when source and destination differ in
+// their position inside a 16-byte line.
+template <int SH>
+__device__ __forceinline__ u32x4 funnel16(u32x4 a, u32x4 b) {
+  constexpr int q = SH / 4, r = SH % 4;
+  const uint32_t c[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (r == 0) {
+      out[i] = c[q + i];
+    } else {
+      out[i] = __builtin_amdgcn_alignbyte(c[q + i + 1], c[q + i], r);  // ({hi, lo} >> 8r), low 32 bits
+    }
   }
-  for (int64_t j = threadIdx.x; j < head; j += kBlock) {
-    const uint16_t x = s[j];
-    d[j] = x;
-    if (ACC) accumulate<DT>(x, acc, bad);
-  }
-  const global_u32x4_ptr sv = (global_u32x4_ptr)(s + head);
-  u32x4* dv = reinterpret_cast<u32x4*>(d + head);
+  return out;
+}
+
+// The 16-byte body of a piece: nv destination vectors dv[0 .. nv).  SH = 0:
+// source vector j is sv[j].  SH > 0: it straddles the aligned 16-byte source
+// blocks sv[j] and sv[j + 1] (both hold bytes of the piece, so neither read
+// leaves the source's pages); adjacent threads read the same blocks, so these
+// loads keep the ordinary cache policy and the second read of a block is
+// served by the cache.
+template <int DT, bool ACC, int SH>
+__device__ __forceinline__ void copy_body(const global_u32x4_ptr sv, u32x4* __restrict__ dv, int64_t nv, double& acc,
+                                          uint32_t& bad) {
   constexpr int kU = 4;  // vectors in flight per thread (more than occupancy is worth here)
+  auto load = [&](int64_t j) -> u32x4 {
+    if constexpr (SH == 0) {
+      return __builtin_nontemporal_load(sv + j);
+    } else {
+      return funnel16<SH>(sv[j], sv[j + 1]);
+    }
+  };
   int64_t j = threadIdx.x;
   for (; j + (kU - 1) * kBlock < nv; j += kU * kBlock) {
     u32x4 w[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) w[u] = __builtin_nontemporal_load(sv + j + u * kBlock);
+    for (int u = 0; u < kU; ++u) w[u] = load(j + u * kBlock);
 #pragma unroll
     for (int u = 0; u < kU; ++u) dv[j + u * kBlock] = w[u];
     if (ACC) {
@@ -618,9 +626,53 @@ __device__ void copy_piece(const uint16_t* __restrict__ s_generic, uint16_t* __r
     }
   }
   for (; j < nv; j += kBlock) {
-    const u32x4 w = __builtin_nontemporal_load(sv + j);
+    const u32x4 w = load(j);
     dv[j] = w;
     if (ACC) accumulate8<DT>(w, acc, bad);
+  }
+}
+
+// A workgroup copies len 16-bit elements from s to d: a scalar head brings d
+// to a 16-byte boundary, the body moves 16-byte vectors (copy_body), a scalar
+// tail finishes.  When source and destination differ in their position
+// inside a 16-byte line, each destination vector is assembled from the two
+// aligned source blocks it straddles.  With ACC the copied values are also
+// squared into acc (fp64) and checked for inf/NaN.  Source reads stream
+// (non-temporal); the shard is stored with ordinary stores: the update reads
+// part of it back from the Infinity Cache right away.  Measured on MI355X
+// against non-temporal stores: the GPT-2 1.5B rank's whole step is 1.2%
+// faster that way (its flatten 3.7%) and the Llama-13B one 0.8-1%, although a
+// plain copy runs 1-2% slower.
+template <int DT, bool ACC>
+__device__ void copy_piece(const uint16_t* __restrict__ s_generic, uint16_t* __restrict__ d, int64_t len, double& acc,
+                           uint32_t& bad) {
+  const global_u16_ptr s = (global_u16_ptr)s_generic;
+  const uintptr_t ds = reinterpret_cast<uintptr_t>(d), ss = reinterpret_cast<uintptr_t>(s_generic);
+  int64_t head = static_cast<int64_t>(((16u - (ds & 15u)) & 15u) >> 1);
+  if (head > len) head = len;
+  const int64_t nv = (len - head) >> 3;
+  for (int64_t j = threadIdx.x; j < head; j += kBlock) {
+    const uint16_t x = s[j];
+    d[j] = x;
+    if (ACC) accumulate<DT>(x, acc, bad);
+  }
+  if (nv > 0) {
+    // byte offset of the body's first source byte inside its 16-byte line:
+    // 0 when the phases match, else even (both are 2-byte aligned)
+    const uintptr_t sb = ss + 2 * static_cast<uintptr_t>(head);
+    const int shift = static_cast<int>(sb & 15u);
+    const global_u32x4_ptr sv = (global_u32x4_ptr)(s_generic + head - shift / 2);  // aligned: sb - shift
+    u32x4* dv = reinterpret_cast<u32x4*>(d + head);
+    switch (shift) {  // uniform across the workgroup
+      case 0: copy_body<DT, ACC, 0>(sv, dv, nv, acc, bad); break;
+      case 2: copy_body<DT, ACC, 2>(sv, dv, nv, acc, bad); break;
+      case 4: copy_body<DT, ACC, 4>(sv, dv, nv, acc, bad); break;
+      case 6: copy_body<DT, ACC, 6>(sv, dv, nv, acc, bad); break;
+      case 8: copy_body<DT, ACC, 8>(sv, dv, nv, acc, bad); break;
+      case 10: copy_body<DT, ACC, 10>(sv, dv, nv, acc, bad); break;
+      case 12: copy_body<DT, ACC, 12>(sv, dv, nv, acc, bad); break;
+      default: copy_body<DT, ACC, 14>(sv, dv, nv, acc, bad); break;
+    }
   }
   for (int64_t t = head + 8 * nv + threadIdx.x; t < len; t += kBlock) {
     const uint16_t x = s[t];

@@ -54,15 +54,18 @@ def test_streaming_update_accesses_are_nontemporal(asm):
 
 
 def test_flatten_uses_global_streaming_reads(asm):
-    """Source reads stream (non-temporal); the shard is written with ordinary stores (the update reads it
-    back next, which measured faster for the whole step)."""
+    """Source reads of the vector body stream (non-temporal) when source and destination share their 16-byte
+    phase: its four unrolled vectors and its remainder loop, at least five wide non-temporal loads.  The
+    phase-shifted bodies read every aligned source block twice (two adjacent threads), so those loads keep the
+    ordinary cache policy on purpose.  The shard is written with ordinary stores (the update reads it back
+    next, which measured faster for the whole step).  No flat (generic) memory instructions."""
     ks = kernels(asm)
     flat = {n: b for n, b in ks.items() if "flatten_kernel" in n}
     assert len(flat) == 3
     for name, body in flat.items():
         assert not [l for l in body if l.startswith("flat_")], f"{name}: flat (not global) memory instructions"
         loads = [l for l in body if re.match(r"global_load_dwordx4\b", l)]
-        assert loads and all(re.search(r"\bnt\b", l) for l in loads), name
+        assert sum(1 for l in loads if re.search(r"\bnt\b", l)) >= 5, name
 
 
 def test_no_scalar_memory_writes_and_no_packed_fp32(asm):
