@@ -64,6 +64,9 @@ MUTATIONS = {
         "  out->bytes_zero1 = 2 * out->padded_numel + 2 * out->padded_numel + 12 * shard;",
         "  out->bytes_zero1 = 2 * out->padded_numel + 12 * shard;"),
     "valid count not clamped to the shard": ("  if (valid > shard) valid = shard;", "  (void)0;"),
+    "underflowed loss scale accepted": ("  if (!flag && !isfinite(total / (scale * scale))) return ORC_ERR_INVALID;",
+                                        "  (void)0;"),
+    "infinite loss scale accepted": ("  if (!isfinite(scale)) return ORC_ERR_INVALID;", "  (void)0;"),
 }
 
 

@@ -191,3 +191,21 @@ def test_step_decision_overflow_skips_and_halves():
     assert dec["skip"] == 1 and dec["loss_scale"] == 32768.0 and dec["good_steps"] == 0
     dec = oracle.step_decision([4.0], [0], 0.0, 1.0, 0, 2**31 - 1)
     assert dec["skip"] == 0 and dec["grad_scale"] == 1.0 and dec["global_norm"] == 2.0
+
+
+def test_step_decision_refuses_an_unusable_loss_scale():
+    """Reading: no decision without a usable loss scale.  IEEE fixes when that happens: the smallest positive
+    double squared is 0 and 1e-170 squared underflows to 0, so a step without overflow has no finite unscaled
+    norm; 1e-150 squared (1e-300) and 2^-537 squared (2^-1074, the smallest subnormal) are still positive."""
+    assert 5e-324 * 5e-324 == 0.0 and 1e-170 * 1e-170 == 0.0
+    assert 1e-150 * 1e-150 > 0.0 and 2.0**-537 * 2.0**-537 == 2.0**-1074
+    for scale in (0.0, -2.0, float("inf"), float("nan"), 5e-324, 1e-170):
+        with pytest.raises(oracle.OracleError):
+            oracle.step_decision([2.5], [0], 1.0, scale, 0, 1000)
+    for scale in (0.0, float("inf")):
+        with pytest.raises(oracle.OracleError):
+            oracle.step_decision([2.5], [1], 1.0, scale, 0, 1000)
+    dec = oracle.step_decision([2.5], [1], 1.0, 5e-324, 4, 1000)  # an overflow is an ordinary skip
+    assert dec["skip"] == 1 and dec["loss_scale"] == 0.0 and dec["good_steps"] == 0
+    dec = oracle.step_decision([2.5e-300], [0], 1.0, 2.0**-537, 0, 1000)
+    assert dec["skip"] == 0 and dec["global_norm"] == pytest.approx(2.5e-300**0.5 / 2.0**-537, rel=1e-15)
