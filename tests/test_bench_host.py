@@ -26,14 +26,16 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in res.stderr and res.stdout == ""
 
 
-def test_traffic_record_is_consistent():
-    """The committed counter record: per-call bytes of the update on the GPT-2 rank shard, scaled by the copy
-    calibration, next to the 28 B/param algorithmic count of that shard."""
+@pytest.mark.parametrize("name", ["llama-13b", "gpt2-1.5b"])
+def test_traffic_record_is_consistent(name):
+    """The committed counter records: per-call bytes of the update on a rank shard (the benchmark's default,
+    Llama-13B, and GPT-2), scaled by the copy calibration, next to the 28 B/param algorithmic count."""
     sys.path.insert(0, ROOT)
     from synth.workloads import WORKLOADS
 
-    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_adamw_tiled_kernel_gpt2-1.5b.json")))
-    w = WORKLOADS["gpt2-1.5b"]
+    rec = json.load(open(os.path.join(ROOT, "profiles", f"traffic_adamw_tiled_kernel_{name}.json")))
+    w = WORKLOADS[name]
+    assert rec["workload"] == name and rec["kernel"] == "adamw_tiled_kernel"
     s = -(-sum(w.numels) // w.world)
     assert rec["shard_numel"] == s and rec["algorithmic_bytes"] == 28 * s
     assert rec["launches_per_call"] == -(-s // 2**25)
