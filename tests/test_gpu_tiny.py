@@ -96,3 +96,58 @@ def test_tiny_all_ranks(mode):
     assert last.layout.shard_valid == s - 1
     for x in last.read_state():
         assert int(x[-1:].view(torch.int32).cpu()[0]) == 0
+
+
+def test_host_decision_on_a_side_stream():
+    """rank_step on a stream other than torch's current one: flatten + norm, the 16-byte readback and the host
+    wait all follow that stream, so the decision sees this step's norms.  The side stream is kept busy first
+    (a few GB of fills), so a readback not ordered after its norm would read the previous step's values."""
+    from mixed_precision_adam_amd.driver import rank_step
+
+    w = WORKLOADS["tiny"]
+    dev = torch.device("cuda:0")
+    src = torch.empty(w.psi, dtype=torch.bfloat16, device=dev)
+    shards = [RankShard(w.numels, w.world, r, Z.ZERO_BF16, dev, sources=[src], tiled=True, fused=True)
+              for r in w.ranks]
+    s = shards[0].n
+    master_all = synth.fill_host(w.master_field(), 0, w.psi)
+    ref = []
+    for sh in shards:
+        lay = sh.layout
+        p = np.zeros(s, np.float32)
+        p[:lay.shard_valid] = master_all[lay.shard_offset:lay.shard_offset + lay.shard_valid]
+        sh.load_master(torch.from_numpy(p).to(dev))
+        ref.append([p, np.zeros(s, np.float32), np.zeros(s, np.float32), np.zeros(s, np.uint16)])
+    cfg = AdamWConfig(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay, max_norm=w.clip)
+    scaler = ScalerState()
+    side = torch.cuda.Stream()
+    busy = torch.empty(1 << 29, dtype=torch.float32, device=dev)
+    oscale, ogood = 1.0, 0
+    for t in (1, 2):
+        synth.fill_tensor(w.grad_field(t), 0, src)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(4):
+                busy.fill_(float(t))
+        dec = rank_step(shards, cfg, scaler, stream=side)
+        side.synchronize()
+        flat_g = synth.fill_host(w.grad_field(t), 0, w.psi)
+        grads = [oracle.flatten([flat_g], w.numels, w.world, r) for r in w.ranks]
+        norms = [oracle.sqnorm(g, oracle.BF16) for g in grads]
+        for r in w.ranks:
+            assert dec["rank_flags"][r] == 0
+            assert_norm_close(dec["rank_sqnorms"][r], norms[r][0], s, f"side stream step {t} rank {r}")
+        od = oracle.step_decision([x[0] for x in norms], [0] * w.world, w.clip, oscale, ogood, 2**31 - 1)
+        oscale, ogood = od["loss_scale"], od["good_steps"]
+        assert dec["skip"] == 0
+        assert_grad_scale_close(dec["grad_scale"], od["grad_scale"], w.world * s, f"side stream step {t}")
+        for r, sh in enumerate(shards):
+            P, M, V, Q = ref[r]
+            oracle.adamw_step(grads[r], oracle.BF16, P, M, V, Q, lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                              weight_decay=w.weight_decay, grad_scale=dec["grad_scale"], step=t)
+            gp, gm, gv = (x.cpu().numpy() for x in sh.read_state())
+            what = f"side stream step {t} rank {r}"
+            nd = assert_f32_close(gp, P, what + " master") + assert_f32_close(gm, M, what + " m")
+            nd += assert_f32_close(gv, V, what + " v")
+            nd += assert_bf16_within_ulp(bits16(sh.param), Q, what + " param")
+            assert nd == 0, what
