@@ -194,13 +194,16 @@ def test_config_parity(name):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,bucket", [("gpt2-1.5b", 0), ("gpt2-1.5b", 1 << 25), ("llama-13b", 0)])
+@pytest.mark.parametrize("name,bucket", [("gpt2-1.5b", 0), ("gpt2-1.5b", 1 << 25), ("llama-7b", 0), ("llama-13b", 0),
+                                         ("1t-zero3", 0)])
 def test_benchmark_path_parity(name, bucket):
     """A rank shard exactly as `bench.py` steps it: fused flatten + norm (in one pass, or in constant-capacity
     buckets of 2^25 elements, last first), the decision on the device, the tiled update in launches of 2^25
-    elements.  GPT-2 1.5B (bf16) and Llama-13B (the benchmark's default: fp16 gradients stored multiplied by
-    a dynamic loss scale that starts at 65536, +inf injected at step 2 and -inf at step 5, so the device
-    skips those steps and halves the scale: 65536 -> 32768 -> 16384 over 4 Adam steps).  The GPU takes its
+    elements.  GPT-2 1.5B (bf16), Llama-7B (bf16 with 0.1% outliers: clipping active), Llama-13B (the
+    benchmark's default: fp16 gradients stored multiplied by a dynamic loss scale that starts at 65536, +inf
+    injected at step 2 and -inf at step 5, so the device skips those steps and halves the scale: 65536 ->
+    32768 -> 16384 over 4 Adam steps) and the 1T ZeRO-3 shard (fp16 gradients in the shard, the norm as its
+    own pass, cosine learning rate over 10 steps).  The GPU takes its
     own decision; the oracle takes its own.  Skip, loss scale, good steps and Adam t must agree exactly and
     the factor within the bound of two fp64 summation orders (several factors are correct).  The update given
     a factor is unique, so the oracle then applies the device's factor and the sampled states must agree bit
@@ -215,10 +218,13 @@ def test_benchmark_path_parity(name, bucket):
     growth = 1000 if gdt == Z.ZERO_FP16 else 2**31 - 1
     lay, segs = Z.zero_shard_layout(w.numels, w.world, rank)
     starts = np.cumsum([0] + list(w.numels))
-    sources = [None] * len(w.numels)
-    for sg in segs:
-        sources[sg.tensor] = torch.empty(w.numels[sg.tensor], dtype=tdt, device=dev)
-    sh = RankShard(w.numels, w.world, rank, gdt, dev, sources=sources, tiled=True, fused=True)
+    flat = w.flat_shard_only  # gradients generated in the shard: no flatten, the norm as its own pass
+    sources = None
+    if not flat:
+        sources = [None] * len(w.numels)
+        for sg in segs:
+            sources[sg.tensor] = torch.empty(w.numels[sg.tensor], dtype=tdt, device=dev)
+    sh = RankShard(w.numels, w.world, rank, gdt, dev, sources=sources, tiled=True, fused=not flat)
     S = sh.n
     master0 = torch.zeros(S, dtype=torch.float32, device=dev)
     synth.fill_tensor(w.master_field(), lay.shard_offset, master0[:lay.shard_valid])
@@ -246,8 +252,17 @@ def test_benchmark_path_parity(name, bucket):
     for t in range(1, w.steps + 1):
         print(f"[{name} bucket={bucket}] step {t}", flush=True)
         field = w.grad_field(t, oscale)  # gradients stored multiplied by the scale in force
-        for sg in segs:
-            synth.fill_tensor(field, int(starts[sg.tensor]), sources[sg.tensor])
+        if flat:
+            sh.grad[lay.shard_valid:].zero_()
+            synth.fill_tensor(field, lay.shard_offset, sh.grad[:lay.shard_valid])
+        else:
+            for sg in segs:
+                synth.fill_tensor(field, int(starts[sg.tensor]), sources[sg.tensor])
+        olr = w.lr
+        if w.lr_min is not None:  # the workload's cosine schedule
+            cfg.lr = Z.zero_cosine_lr(t, w.steps, w.lr, w.lr_min)
+            olr = oracle.cosine_lr(t, w.steps, w.lr, w.lr_min)
+            assert cfg.lr == olr
         inject_at = None
         if t in w.inject:
             val, frac = w.inject[t]
@@ -258,7 +273,10 @@ def test_benchmark_path_parity(name, bucket):
             sg = next(x for x in segs if x.dst_offset <= j < x.dst_offset + x.numel)
             sources[sg.tensor].view(torch.int16)[sg.src_offset + j - sg.dst_offset] = hb - (1 << 16 if hb >= 1 << 15
                                                                                               else 0)
-        runner.step()
+        if bucket:
+            runner.step()
+        else:
+            runner.step(flatten=not flat)
         st = runner.read()
         g_host = host_shard_grads(w, field, lay, inject_at)
         for a, b in wins:
@@ -282,7 +300,7 @@ def test_benchmark_path_parity(name, bucket):
         for (a, b), R in zip(wins, ref):
             if not od["skip"]:  # ... and the update given that factor is unique: the oracle applies it too
                 g_win = host_shard_grads_window(w, field, lay, a, b, inject_at)
-                oracle.adamw_step(g_win, gdt, R[0], R[1], R[2], R[3], lr=w.lr, beta1=w.beta1, beta2=w.beta2,
+                oracle.adamw_step(g_win, gdt, R[0], R[1], R[2], R[3], lr=olr, beta1=w.beta1, beta2=w.beta2,
                                   eps=w.eps, weight_decay=w.weight_decay, grad_scale=st["grad_scale"], step=ostep)
             gp, gm, gv = (x.cpu().numpy() for x in sh.state_views(a, b))
             ww = f"{what} [{a},{b})"
