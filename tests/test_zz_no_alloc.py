@@ -91,3 +91,51 @@ def test_noalloc_rejects_bad_arguments_without_launching():
     assert lib.zero_flatten_grads_sqnorm_noalloc(16, 1, 0, 16, 8, 12, 16, None) == Z.ZERO_ERR_INVALID  # misaligned
     assert lib.zero_flatten_grads_sqnorm_noalloc(16, 1, 5, 16, 8, 16, 24, None) == Z.ZERO_ERR_INVALID  # dtype
     assert lib.zero_flatten_grads_sqnorm_noalloc(None, 1, 0, 16, 8, 16, 24, None) == Z.ZERO_ERR_INVALID
+
+
+def test_noalloc_captured_in_a_graph_matches_eager_calls():
+    """The use it exists for: a HIP graph that captures the allocation-free call (nothing is allocated during
+    capture) and is replayed after fresh gradients are written eagerly, with the host synchronising in
+    between.  Every replay must equal the workspace entry point run eagerly on the same gradients, bit for
+    bit; the first call on the device happens eagerly, before capture."""
+    numels, world, rank = [70_001, 3, 1_000_000, 4096], 2, 1
+    lay, segs = Z.zero_shard_layout(numels, world, rank)
+    starts = np.cumsum([0] + numels)
+    srcs = [torch.empty(k, dtype=torch.bfloat16, device=DEV) for k in numels]
+    table = torch.frombuffer(bytearray(Z.zero_flatten_plan(segs, srcs)), dtype=torch.uint8).to(DEV)
+    n = lay.shard_numel
+    ws_bytes = Z.zero_grad_sqnorm_workspace_bytes(n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    shard_g = torch.zeros(n, dtype=torch.int16, device=DEV)
+    out_g = torch.zeros(2, dtype=torch.float64, device=DEV)
+    shard_e = torch.zeros(n, dtype=torch.int16, device=DEV)
+    out_e = torch.zeros(2, dtype=torch.float64, device=DEV)
+
+    def fill(t):
+        f = synth.field(0x5EED0104, synth.STREAM_GRAD, t, 1e-3, synth.BF16)
+        for k, src in enumerate(srcs):
+            synth.fill_tensor(f, int(starts[k]), src)
+
+    fill(0)
+    Z.zero_flatten_grads_sqnorm_noalloc(table, len(segs), Z.ZERO_BF16, shard_g, n, out_g.data_ptr(),
+                                        out_g.data_ptr() + 8)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        Z.zero_flatten_grads_sqnorm_noalloc(table, len(segs), Z.ZERO_BF16, shard_g, n, out_g.data_ptr(),
+                                            out_g.data_ptr() + 8)
+    for t in range(1, 5):
+        fill(t)
+        if t == 3:
+            srcs[2].view(torch.int16)[900_000] = 0x7F80  # +inf inside rank 1's shard, this replay only
+        torch.cuda.synchronize()
+        Z.zero_flatten_grads_sqnorm(table, len(segs), Z.ZERO_BF16, shard_e, n, ws, ws_bytes, out_e.data_ptr(),
+                                    out_e.data_ptr() + 8)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(shard_g, shard_e), t
+        he, hg = out_e.cpu().numpy(), out_g.cpu().numpy()
+        assert hg[1:].view(np.int32)[0] == he[1:].view(np.int32)[0] == (1 if t == 3 else 0), t
+        if t != 3:
+            assert hg[:1].view(np.uint64)[0] == he[:1].view(np.uint64)[0], (t, hg[0], he[0])
