@@ -112,6 +112,23 @@ void decisions_and_sizes() {
     CHECK(zero_grad_sqnorm_workspace_bytes(m) >= 12u * static_cast<uint64_t>(zero_flatten_partials_count(m)));
   }
   CHECK(zero_grad_sqnorm_workspace_bytes(INT64_MAX) <= 12u * (1u << 19) + 256u);
+  // loss scales down to the smallest subnormal: refused exactly when the scale is unusable or, without an
+  // overflow, the unscaled square-norm is not finite; refused calls write nothing
+  for (int trial = 0; trial < 5000; ++trial) {
+    double sq = static_cast<double>(below(1000000)) * 1e-3;
+    int32_t fl = below(4) == 0;
+    double scale = std::ldexp(1.0, -static_cast<int>(below(1080)));
+    if (below(50) == 0) scale = below(2) ? 0.0 : HUGE_VAL;
+    const double scale0 = scale;
+    double gs = -7.0, norm = -7.0;
+    int32_t good = 5, skip = -7;
+    const bool usable = std::isfinite(scale) && scale > 0.0 && (fl || std::isfinite(sq / (scale * scale)));
+    const int rc = zero_step_decision(&sq, &fl, 1, 1.0, &scale, &good, 1000, &gs, &skip, &norm);
+    CHECK(rc == (usable ? ZERO_OK : ZERO_ERR_INVALID));
+    if (!usable) CHECK(scale == scale0 && good == 5 && skip == -7 && gs == -7.0 && norm == -7.0);
+    if (usable && fl) CHECK(skip == 1 && scale == scale0 * 0.5 && good == 0);
+    if (usable && !fl) CHECK(skip == 0 && std::isfinite(gs));
+  }
 }
 
 void device_argument_checks() {
@@ -141,6 +158,19 @@ void device_argument_checks() {
   CHECK(zero_step_decision_dev(nullptr, nullptr, 1, 1.0, &hp, nullptr, nullptr) == ZERO_ERR_INVALID);
   CHECK(zero_state_tile(nullptr, nullptr, nullptr, nullptr, 8, nullptr) == ZERO_ERR_INVALID);
   CHECK(zero_state_untile(nullptr, nullptr, nullptr, nullptr, -1, nullptr) == ZERO_ERR_INVALID);
+  alignas(16) static double d2[2];
+  CHECK(zero_flatten_grads_sqnorm_noalloc(nullptr, 1, ZERO_BF16, h, 8, d2, reinterpret_cast<int32_t*>(d2 + 1),
+                                          nullptr) == ZERO_ERR_INVALID);
+  CHECK(zero_flatten_grads_sqnorm_noalloc(nullptr, 0, ZERO_BF16, h, 8, nullptr, nullptr, nullptr) ==
+        ZERO_ERR_INVALID);
+  CHECK(zero_flatten_grads_sqnorm_noalloc(nullptr, 0, static_cast<zero_dtype>(9), h, 8, d2,
+                                          reinterpret_cast<int32_t*>(d2 + 1), nullptr) == ZERO_ERR_INVALID);
+  CHECK(zero_flatten_grads_sqnorm_noalloc(nullptr, 0, ZERO_BF16, h, 8, reinterpret_cast<double*>(h + 1),
+                                          reinterpret_cast<int32_t*>(d2 + 1), nullptr) == ZERO_ERR_INVALID);
+  CHECK(zero_calibrate_tiled_rmw(h, f, h, -1, 0u, nullptr) == ZERO_ERR_INVALID);
+  CHECK(zero_calibrate_tiled_rmw(h, f + 1, h, 8, 0u, nullptr) == ZERO_ERR_INVALID);
+  CHECK(zero_calibrate_tiled_rmw(nullptr, f, h, 8, 0u, nullptr) == ZERO_ERR_INVALID);
+  CHECK(zero_calibrate_tiled_rmw(nullptr, nullptr, nullptr, 0, 0u, nullptr) == ZERO_OK);
 }
 
 }  // namespace
